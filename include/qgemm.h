@@ -1,0 +1,193 @@
+/*
+ * qgemm: weight-only-int4 GEMMs and the int8 vocabulary-table kernels for
+ * MI355X (gfx950), as a plain C ABI.
+ *
+ * Sources (pages cited by title and section):
+ *   [OPT]  "What this repo does that stock vLLM doesn't" (the project's
+ *          optimisations page), "In full" items 1, 2, 4, 5 and the section
+ *          "int8 prefill for single-user mode".
+ *   [README] the project README, section "What each step buys".
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after returning.
+ *   - Device pointers must be 16-byte aligned; leading dimensions are in
+ *     elements and must keep every row 16-byte aligned (ldx % 8 == 0 for
+ *     fp16 rows).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it asynchronously; no call synchronises the
+ *     host.  Outputs are valid once that stream reaches the enqueued work.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     an error nothing is launched, nothing is written and the status code
+ *     says why.  No entry point aborts or throws.
+ *   - Row-major layouts.  fp16 is IEEE binary16, stored as uint16.
+ *   - Calls that share a workspace buffer must be ordered on one stream.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics; every reduction runs in a fixed order).
+ *
+ * Weight format (int4 body, [OPT] "In full" item 4)
+ *   Canonical weights are codes[N][K] (int8 storage, values in [-8, 7], the
+ *   two's complement int4 range) and signed fp16 group scales
+ *   scales[N][K/128]: w[n][k] = codes[n][k] * scales[n][k/128].  Negative
+ *   scales are honoured as they are (no sign is folded into the codes).
+ *   w4_repack turns them into the opaque pre-shuffled layout the GEMMs read.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning entry point. */
+#define QG_OK 0
+#define QG_ERR_INVALID_ARG 1       /* null/misaligned pointer, negative size, ldx < K, bad op */
+#define QG_ERR_UNSUPPORTED_SHAPE 2 /* K % 128 != 0, N % 16 != 0, H % 128 != 0, size too large */
+#define QG_ERR_WORKSPACE 3         /* ws_bytes smaller than qg_workspace_bytes() */
+#define QG_ERR_LAUNCH 4            /* the HIP runtime reported an error at launch */
+
+/* Operation ids for qg_workspace_bytes. */
+#define QG_OP_W4A16 1
+#define QG_OP_W4A8 2
+#define QG_OP_W8A16 3
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* qg_status_string(int status);
+
+/* The HIP runtime's description of the error behind the calling thread's
+ * most recent QG_ERR_LAUNCH ("none" if there was none).  Thread-local; the
+ * pointer stays valid for the life of the process. */
+const char* qg_last_hip_error(void);
+
+/* Bytes of the packed weight / packed scale buffers w4_repack writes for an
+ * [N, K] weight.  0 if the shape is unsupported. */
+size_t w4_packed_bytes(int64_t N, int64_t K);
+size_t w4_scales_bytes(int64_t N, int64_t K);
+
+/* Bytes of device workspace the GEMM `op` needs for this shape (0 is a valid
+ * answer: no workspace needed).  Returns (size_t)-1 for an invalid op or
+ * shape.  The workspace holds the int8 activation codes and token scales of
+ * W4A8 and the fp32 split-K partial sums; it needs no initialisation and its
+ * contents after a call are unspecified. */
+size_t qg_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
+
+/*
+ * act_quant_int8 -- per-token int8 activation quantisation ([OPT] "In full"
+ * item 4: activations are quantised to int8 per token).
+ *   x      fp16 [M][ldx] (first K columns used), ldx >= K, ldx % 8 == 0
+ *   q      int8 [M][K] out:  q[m][k] = clamp(rne(fp32(x[m][k]) / scale[m]), -127, 127)
+ *   scale  fp32 [M]    out:  scale[m] = fp32(max_k |x[m][k]|) / 127 (IEEE division);
+ *                            a row of zeros gets scale 0 and codes 0.
+ *   M >= 0, K > 0 and K % 128 == 0.  Codes and scales are bit-exact against
+ *   that definition.  NaN/Inf inputs give unspecified codes.
+ */
+int act_quant_int8(const void* x_f16, int64_t M, int64_t K, int64_t ldx,
+                   int8_t* q, float* scale, void* stream);
+
+/*
+ * w4_repack -- load-time reshuffle of canonical int4 weights into the layout
+ * the GEMMs stream with 128-bit loads ([OPT] "In full" item 4).
+ *   codes     int8 [N][K], values in [-8, 7] (only the low 4 bits are used)
+ *   scales    fp16 [N][K/128], signed
+ *   w_packed  out, w4_packed_bytes(N, K) bytes (K*N/2)
+ *   s_packed  out, w4_scales_bytes(N, K) bytes (same size as scales)
+ *   N % 16 == 0, K % 128 == 0.  Not a sign fold: codes and scales keep
+ *   their signs.  One packed buffer serves both w4a16_gemm and w4a8_gemm.
+ */
+int w4_repack(const int8_t* codes, const void* scales_f16, int64_t N, int64_t K,
+              void* w_packed, void* s_packed, void* stream);
+
+/*
+ * w4a16_gemm -- y = x * W^T with int4 weights and fp16 activations ([README]
+ * "What each step buys": the W4A16 body; used for decode and speculative
+ * verify, M = 1 + draft tokens).
+ *   x         fp16 [M][ldx]
+ *   w_packed, s_packed  from w4_repack for [N, K]
+ *   y         fp16 [M][N] out: y[m][n] = fp16(sum_k x[m][k] * codes[n][k] * scales[n][k/128]),
+ *             products of fp16 x and exact int4 codes accumulated in fp32,
+ *             each 128-wide group rescaled by its fp32 scale.
+ *   workspace  >= qg_workspace_bytes(QG_OP_W4A16, M, K, N) bytes (may be
+ *             NULL when that is 0)
+ */
+int w4a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
+               const void* w_packed, const void* s_packed, void* y_f16,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * w4a8_gemm -- W4A8: per-token int8 activations times int4 weights on the
+ * int8 matrix cores ([OPT] "In full" item 4 and "int8 prefill for
+ * single-user mode").  Quantises x inside the call (as act_quant_int8, into
+ * the workspace), then
+ *   P[m][n][g] = sum_{j<128} q[m][128g+j] * codes[n][128g+j]   (exact int32)
+ *   y[m][n]    = fp16(scale[m] * sum_g fp32(P[m][n][g]) * scales[n][g])   (fp32)
+ * Same arguments as w4a16_gemm; the workspace must hold
+ * qg_workspace_bytes(QG_OP_W4A8, M, K, N) bytes.
+ */
+int w4a8_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
+              const void* w_packed, const void* s_packed, void* y_f16,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * w4a8_gemm_debug -- w4a8_gemm that also exposes its integer stages, for
+ * bit-exact checks.  Runs the same kernels as w4a8_gemm and in addition
+ * writes
+ *   q_out     int8 [M][K]   the activation codes   (may be NULL)
+ *   scale_out fp32 [M]      the token scales       (may be NULL)
+ *   partials  int32 [m1-m0][n1-n0][K/128]  P[m][n][g] for m0 <= m < m1,
+ *             n0 <= n < n1, at index ((m-m0)*(n1-n0) + (n-n0))*(K/128) + g
+ *             (may be NULL; then the window is ignored)
+ *   0 <= m0 <= m1 <= M, 0 <= n0 <= n1 <= N.
+ */
+int w4a8_gemm_debug(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
+                    const void* w_packed, const void* s_packed, void* y_f16,
+                    void* workspace, size_t ws_bytes, void* stream,
+                    int8_t* q_out, float* scale_out, int32_t* partials,
+                    int64_t m0, int64_t m1, int64_t n0, int64_t n1);
+
+/*
+ * w8a16_gemm -- the int8-weight lm_head product over the same row-major
+ * table the embedding gather reads ([OPT] "In full" items 1 and 5).
+ *   w   int8 [N][K] row-major (the vocabulary table, N = V rows, K = H)
+ *   s   fp16 [N][K/128] (its group scales)
+ *   y   fp16 [M][N] out: y[m][n] = fp16(sum_k x[m][k] * w[n][k] * s[n][k/128])
+ *       (fp32 accumulation, per-group fp32 rescale)
+ *   Other arguments as w4a16_gemm; op id QG_OP_W8A16 for the workspace.
+ */
+int w8a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
+               const int8_t* w, const void* s_f16, void* y_f16,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * embed_gather_dequant_int8 -- dequant-on-gather embedding lookup ([OPT]
+ * "In full" item 2).
+ *   ids     int32 [T]
+ *   table   int8 [V][H], scales fp16 [V][H/128]
+ *   out     fp16 [T][H]: out[t][h] = fp16(fp32(table[id][h]) * fp32(scales[id][h/128]))
+ *           (one rounding: the fp32 product is exact).  An id outside
+ *           [0, V) gives a row of zeros.
+ *   T >= 0, V > 0, H % 128 == 0.
+ */
+int embed_gather_dequant_int8(const int32_t* ids, int64_t T, const int8_t* table,
+                              const void* scales_f16, int64_t V, int64_t H,
+                              void* out_f16, void* stream);
+
+/*
+ * quant_table_int8 -- the offline requantisation of a bf16 vocabulary table
+ * to int8 group-128 ([OPT] "In full" item 1), on the device.
+ *   src   bf16 [V][H] (uint16 bit patterns)
+ *   Q     int8 [V][H] out, S fp16 [V][H/128] out:
+ *         S = fp16(fp32(absmax of the group) / 127),
+ *         Q = clamp(rne(fp32(src) / fp32(S)), -127, 127), and Q = 0 where S == 0.
+ *   H % 128 == 0.  Bit-exact against that definition.
+ */
+int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H,
+                     int8_t* Q, void* S_f16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

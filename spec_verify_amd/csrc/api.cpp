@@ -1,0 +1,283 @@
+// C-ABI entry points of libqgemm: host-side validation, workspace layout and
+// dispatch to the gfx950 kernels.  Nothing here allocates device memory or
+// synchronises the host; every check happens before the first launch.
+#include "qgemm.h"
+
+#include <stdint.h>
+
+#include "common.h"
+
+namespace {
+
+using qg::kGroup;
+
+constexpr int64_t kMaxDim = INT32_MAX;     // kernels index rows/columns with 32-bit ints
+constexpr int64_t kSkinnyMaxM = 64;         // largest M the weight-streaming kernel takes per launch
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// HIP error behind the calling thread's most recent QG_ERR_LAUNCH.
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+inline int launch_status(hipError_t e) {
+  if (e == hipSuccess) return QG_OK;
+  t_last_hip_error = e;
+  return QG_ERR_LAUNCH;
+}
+
+// hipGetLastError reports the thread's last error from any earlier runtime
+// call, not only from our launches; drop such a stale error before launching
+// so that a launch is judged by its own result.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// Shape checks shared by the three GEMMs.
+int check_gemm_shape(int64_t M, int64_t K, int64_t N, int64_t ldx) {
+  if (M < 0 || K <= 0 || N <= 0) return QG_ERR_INVALID_ARG;
+  if (K % kGroup != 0 || N % 16 != 0) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < K || ldx % 8 != 0) return QG_ERR_INVALID_ARG;
+  return QG_OK;
+}
+
+int check_ptrs(int64_t M, const void* x, const void* w, const void* s, const void* y) {
+  if (M == 0) return QG_OK;
+  if (!x || !w || !s || !y) return QG_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(y)) return QG_ERR_INVALID_ARG;
+  return QG_OK;
+}
+
+// Workspace layout of w4a8_gemm: int8 codes [M][K], fp32 token scales [M],
+// then fp32 split-K partial sums [splits][M][N] for the weight-streaming
+// kernel.  Each region starts on a 256-byte boundary.
+struct W4A8Layout {
+  size_t q_off, s_off, p_off, total;
+};
+
+W4A8Layout w4a8_layout(int64_t M, int64_t K, int64_t N) {
+  W4A8Layout L;
+  L.q_off = 0;
+  L.s_off = round_up((size_t)M * (size_t)K, 256);
+  L.p_off = round_up(L.s_off + (size_t)M * 4, 256);
+  size_t part = 0;
+  if (M <= kSkinnyMaxM) {
+    const int s = qg::skinny_splits(N, K);
+    if (s > 1) part = (size_t)s * (size_t)M * (size_t)N * 4;
+  }
+  L.total = L.p_off + part;
+  return L;
+}
+
+// Partial-sum bytes of w4a16_gemm / w8a16_gemm (they run M in chunks of 64).
+size_t streaming_partials_bytes(int64_t M, int64_t K, int64_t N) {
+  const int s = qg::skinny_splits(N, K);
+  if (s <= 1 || M == 0) return 0;
+  const int64_t mc = M < kSkinnyMaxM ? M : kSkinnyMaxM;
+  return (size_t)s * (size_t)mc * (size_t)N * 4;
+}
+
+int gemm_streaming(int mode, const void* x, int64_t M, int64_t K, int64_t N, int64_t ldx,
+                   const void* w, const void* s, void* y, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_gemm_shape(M, K, N, ldx);
+  if (st != QG_OK) return st;
+  if ((st = check_ptrs(M, x, w, s, y)) != QG_OK) return st;
+  if (M == 0) return QG_OK;
+  const size_t need = streaming_partials_bytes(M, K, N);
+  if (need > 0 && (!ws || ws_bytes < need)) return QG_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  for (int64_t m0 = 0; m0 < M; m0 += kSkinnyMaxM) {
+    qg::SkinnyArgs a = {};
+    a.mode = mode;
+    a.act = reinterpret_cast<const uint16_t*>(x) + m0 * ldx;
+    a.lda = ldx;
+    a.tok_scale = nullptr;
+    a.w = w;
+    a.s = reinterpret_cast<const uint16_t*>(s);
+    a.M = (M - m0) < kSkinnyMaxM ? (M - m0) : kSkinnyMaxM;
+    a.N = N;
+    a.K = K;
+    a.y = reinterpret_cast<uint16_t*>(y) + m0 * N;
+    a.partials = reinterpret_cast<float*>(ws);
+    a.dbg = nullptr;
+    st = launch_status(qg::launch_skinny(a, as_stream(stream)));
+    if (st != QG_OK) return st;
+  }
+  return QG_OK;
+}
+
+int w4a8_impl(const void* x, int64_t M, int64_t K, int64_t N, int64_t ldx, const void* w_packed,
+              const void* s_packed, void* y, void* ws, size_t ws_bytes, void* stream, int8_t* q_out,
+              float* scale_out, int32_t* partials, int64_t m0, int64_t m1, int64_t n0, int64_t n1) {
+  int st = check_gemm_shape(M, K, N, ldx);
+  if (st != QG_OK) return st;
+  if ((st = check_ptrs(M, x, w_packed, s_packed, y)) != QG_OK) return st;
+  if (partials && !(0 <= m0 && m0 <= m1 && m1 <= M && 0 <= n0 && n0 <= n1 && n1 <= N))
+    return QG_ERR_INVALID_ARG;
+  if (M == 0) return QG_OK;
+  const W4A8Layout L = w4a8_layout(M, K, N);
+  if (!ws || ws_bytes < L.total) return QG_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QG_ERR_INVALID_ARG;
+  if ((q_out && !aligned16(q_out)) || (partials && (reinterpret_cast<uintptr_t>(partials) & 3u)) ||
+      (scale_out && (reinterpret_cast<uintptr_t>(scale_out) & 3u)))
+    return QG_ERR_INVALID_ARG;
+
+  char* base = reinterpret_cast<char*>(ws);
+  int8_t* q = reinterpret_cast<int8_t*>(base + L.q_off);
+  float* ts = reinterpret_cast<float*>(base + L.s_off);
+  hipStream_t hs = as_stream(stream);
+  int32_t* dbg = (partials && m1 > m0 && n1 > n0) ? partials : nullptr;
+
+  clear_stale_error();
+  st = launch_status(qg::launch_act_quant(reinterpret_cast<const uint16_t*>(x), M, K, ldx, q, K, ts, hs));
+  if (st != QG_OK) return st;
+  if (M <= kSkinnyMaxM) {
+    qg::SkinnyArgs a = {};
+    a.mode = qg::kW4A8;
+    a.act = q;
+    a.lda = K;
+    a.tok_scale = ts;
+    a.w = w_packed;
+    a.s = reinterpret_cast<const uint16_t*>(s_packed);
+    a.M = M; a.N = N; a.K = K;
+    a.y = reinterpret_cast<uint16_t*>(y);
+    a.partials = reinterpret_cast<float*>(base + L.p_off);
+    a.dbg = dbg;
+    a.dm0 = m0; a.dm1 = m1; a.dn0 = n0; a.dn1 = n1;
+    st = launch_status(qg::launch_skinny(a, hs));
+  } else {
+    qg::LargeArgs a = {};
+    a.codes = q;
+    a.tok_scale = ts;
+    a.w = w_packed;
+    a.s = reinterpret_cast<const uint16_t*>(s_packed);
+    a.M = M; a.N = N; a.K = K;
+    a.y = reinterpret_cast<uint16_t*>(y);
+    a.dbg = dbg;
+    a.dm0 = m0; a.dm1 = m1; a.dn0 = n0; a.dn1 = n1;
+    st = launch_status(qg::launch_w4a8_large(a, hs));
+  }
+  if (st != QG_OK) return st;
+  if (q_out && (st = launch_status(hipMemcpyAsync(q_out, q, (size_t)M * K, hipMemcpyDeviceToDevice, hs))) != QG_OK)
+    return st;
+  if (scale_out &&
+      (st = launch_status(hipMemcpyAsync(scale_out, ts, (size_t)M * 4, hipMemcpyDeviceToDevice, hs))) != QG_OK)
+    return st;
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(int status) {
+  switch (status) {
+    case QG_OK: return "ok";
+    case QG_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative size, ldx, window or op)";
+    case QG_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (K and H must be multiples of 128, N of 16)";
+    case QG_ERR_WORKSPACE: return "workspace smaller than qg_workspace_bytes()";
+    case QG_ERR_LAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* qg_last_hip_error(void) {
+  return t_last_hip_error == hipSuccess ? "none" : hipGetErrorString(t_last_hip_error);
+}
+
+size_t w4_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 16 || K % kGroup || N > kMaxDim || K > kMaxDim) return 0;
+  return (size_t)N * (size_t)K / 2;
+}
+
+size_t w4_scales_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 16 || K % kGroup || N > kMaxDim || K > kMaxDim) return 0;
+  return (size_t)N * (size_t)(K / kGroup) * 2;
+}
+
+size_t qg_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
+  if (check_gemm_shape(M, K, N, K + (8 - K % 8) % 8) != QG_OK) return (size_t)-1;
+  switch (op) {
+    case QG_OP_W4A8: return M == 0 ? 0 : w4a8_layout(M, K, N).total;
+    case QG_OP_W4A16:
+    case QG_OP_W8A16: return streaming_partials_bytes(M, K, N);
+    default: return (size_t)-1;
+  }
+}
+
+int act_quant_int8(const void* x_f16, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* scale,
+                   void* stream) {
+  if (M < 0 || K <= 0) return QG_ERR_INVALID_ARG;
+  if (K % kGroup != 0 || M > kMaxDim || K > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < K || ldx % 8 != 0) return QG_ERR_INVALID_ARG;
+  if (M == 0) return QG_OK;
+  if (!x_f16 || !q || !scale || !aligned16(x_f16) || !aligned16(q) || !aligned16(scale))
+    return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_act_quant(reinterpret_cast<const uint16_t*>(x_f16), M, K, ldx, q, K,
+                                            scale, as_stream(stream)));
+}
+
+int w4_repack(const int8_t* codes, const void* scales_f16, int64_t N, int64_t K, void* w_packed,
+              void* s_packed, void* stream) {
+  if (N <= 0 || K <= 0) return QG_ERR_INVALID_ARG;
+  if (N % 16 || K % kGroup || N > kMaxDim || K > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (!codes || !scales_f16 || !w_packed || !s_packed) return QG_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales_f16) || !aligned16(w_packed) || !aligned16(s_packed))
+    return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_w4_repack(codes, reinterpret_cast<const uint16_t*>(scales_f16), N, K,
+                                            w_packed, reinterpret_cast<uint16_t*>(s_packed),
+                                            as_stream(stream)));
+}
+
+int w4a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const void* w_packed,
+               const void* s_packed, void* y_f16, void* workspace, size_t ws_bytes, void* stream) {
+  return gemm_streaming(qg::kW4A16, x_f16, M, K, N, ldx, w_packed, s_packed, y_f16, workspace, ws_bytes,
+                        stream);
+}
+
+int w4a8_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const void* w_packed,
+              const void* s_packed, void* y_f16, void* workspace, size_t ws_bytes, void* stream) {
+  return w4a8_impl(x_f16, M, K, N, ldx, w_packed, s_packed, y_f16, workspace, ws_bytes, stream, nullptr,
+                   nullptr, nullptr, 0, 0, 0, 0);
+}
+
+int w4a8_gemm_debug(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const void* w_packed,
+                    const void* s_packed, void* y_f16, void* workspace, size_t ws_bytes, void* stream,
+                    int8_t* q_out, float* scale_out, int32_t* partials, int64_t m0, int64_t m1, int64_t n0,
+                    int64_t n1) {
+  return w4a8_impl(x_f16, M, K, N, ldx, w_packed, s_packed, y_f16, workspace, ws_bytes, stream, q_out,
+                   scale_out, partials, m0, m1, n0, n1);
+}
+
+int w8a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const int8_t* w,
+               const void* s_f16, void* y_f16, void* workspace, size_t ws_bytes, void* stream) {
+  return gemm_streaming(qg::kW8A16, x_f16, M, K, N, ldx, w, s_f16, y_f16, workspace, ws_bytes, stream);
+}
+
+int embed_gather_dequant_int8(const int32_t* ids, int64_t T, const int8_t* table, const void* scales_f16,
+                              int64_t V, int64_t H, void* out_f16, void* stream) {
+  if (T < 0 || V <= 0 || H <= 0) return QG_ERR_INVALID_ARG;
+  if (H % kGroup || V > kMaxDim || H > kMaxDim || T > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return QG_OK;
+  if (!ids || !table || !scales_f16 || !out_f16) return QG_ERR_INVALID_ARG;
+  if (!aligned16(ids) || !aligned16(table) || !aligned16(scales_f16) || !aligned16(out_f16))
+    return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_gather(ids, T, table, reinterpret_cast<const uint16_t*>(scales_f16), V, H,
+                                         reinterpret_cast<uint16_t*>(out_f16), as_stream(stream)));
+}
+
+int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H, int8_t* Q, void* S_f16, void* stream) {
+  if (V <= 0 || H <= 0) return QG_ERR_INVALID_ARG;
+  if (H % kGroup || V > kMaxDim || H > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (!src_bf16 || !Q || !S_f16) return QG_ERR_INVALID_ARG;
+  if (!aligned16(src_bf16) || !aligned16(Q) || !aligned16(S_f16)) return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_quant_table(src_bf16, V, H, Q, reinterpret_cast<uint16_t*>(S_f16),
+                                              as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Internal helpers shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kGroup = 128;        // weight / table group width along K
+constexpr int kWave = 64;          // CDNA wavefront width
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined next to their kernels).  Shapes are validated by
+// the C-ABI layer before any of these is called.
+// ---------------------------------------------------------------------------
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            int8_t* q, int64_t ldq, float* scale, hipStream_t st);
+
+hipError_t launch_w4_repack(const int8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
+                            void* w_packed, uint16_t* s_packed, hipStream_t st);
+
+// Operating modes of the skinny (M <= 64) GEMM kernel.
+enum SkinnyMode { kW4A8 = 0, kW4A16 = 1, kW8A16 = 2 };
+
+// Split-K factor the skinny kernel uses for an [*, K] x [N, K] product; a
+// pure function of (N, K) so workspace sizing and launch agree.
+int skinny_splits(int64_t N, int64_t K);
+
+struct SkinnyArgs {
+  int mode;
+  const void* act;          // W4A8: int8 codes [M][lda]; W4A16 / W8A16: fp16 [M][lda]
+  int64_t lda;
+  const float* tok_scale;   // W4A8 token scales [M]
+  const void* w;            // packed int4 (W4A8/W4A16) or row-major int8 [N][K] (W8A16)
+  const uint16_t* s;        // packed scales (W4A*) or row-major fp16 [N][K/128] (W8A16)
+  int64_t M, N, K;
+  uint16_t* y;              // fp16 [M][N]
+  float* partials;          // [splits][M][N] fp32 when splits > 1
+  int32_t* dbg;             // W4A8 debug window (may be null)
+  int64_t dm0, dm1, dn0, dn1;
+};
+hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
+
+struct LargeArgs {
+  const int8_t* codes;      // [M][K]
+  const float* tok_scale;   // [M]
+  const void* w;            // packed int4
+  const uint16_t* s;        // packed scales
+  int64_t M, N, K;
+  uint16_t* y;
+  int32_t* dbg;
+  int64_t dm0, dm1, dn0, dn1;
+};
+hipError_t launch_w4a8_large(const LargeArgs& a, hipStream_t st);
+
+hipError_t launch_gather(const int32_t* ids, int64_t T, const int8_t* table, const uint16_t* scales,
+                         int64_t V, int64_t H, uint16_t* out, hipStream_t st);
+
+hipError_t launch_quant_table(const uint16_t* src, int64_t V, int64_t H, int8_t* Q, uint16_t* S,
+                              hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);   // v_cvt_f16_f32, round to nearest even
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace qg

@@ -1,0 +1,119 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, sizes buffers as documented and rejects bad arguments with
+the documented status before launching anything (CPU only: every call here
+fails validation, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import spec_verify_amd as qg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qgemm.h")
+
+FAKE = ctypes.c_void_p(1 << 20)           # aligned, never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 8)      # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\(", src, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) == 13, names
+    for n in names:
+        assert hasattr(qg.lib, n), n
+    assert set(names) == set(qg.EXPORTS)
+
+
+def test_status_strings():
+    assert qg.qg_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert qg.qg_status_string(s) and qg.qg_status_string(s) != "unknown status"
+    assert qg.qg_status_string(99) == "unknown status"
+
+
+def test_size_helpers():
+    assert qg.w4_packed_bytes(5120, 5120) == 5120 * 5120 // 2
+    assert qg.w4_scales_bytes(5120, 5120) == 5120 * 40 * 2
+    assert qg.w4_packed_bytes(5120, 100) == 0 and qg.w4_packed_bytes(17, 128) == 0
+    big = qg.qg_workspace_bytes(qg.QG_OP_W4A8, 4096, 17408, 5120)
+    assert big >= 4096 * 17408 + 4096 * 4
+    dec = qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 5120, 5120)
+    assert dec >= 64 * 5120 + 64 * 4
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 0, 5120, 5120) == 0
+    assert qg.qg_workspace_bytes(7, 1, 128, 16) == 2 ** 64 - 1
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 1, 100, 16) == 2 ** 64 - 1
+    # the streaming GEMMs run M in chunks of 64, so their workspace stops growing at 64
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 64, 5120, 5120) == qg.qg_workspace_bytes(qg.QG_OP_W4A16, 640, 5120, 5120)
+
+
+GEMMS = ["w4a16_gemm", "w4a8_gemm", "w8a16_gemm"]
+
+
+def call_gemm(name, M=4, K=256, N=32, ldx=None, x=FAKE, w=FAKE, s=FAKE, y=FAKE, ws=None, wsb=0):
+    f = getattr(qg.lib, name)
+    return f(x, M, K, N, K if ldx is None else ldx, w, s, y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name", GEMMS)
+def test_gemm_shape_errors(name):
+    assert call_gemm(name, K=200) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert call_gemm(name, N=40) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert call_gemm(name, M=-1) == qg.QG_ERR_INVALID_ARG
+    assert call_gemm(name, K=0) == qg.QG_ERR_INVALID_ARG
+    assert call_gemm(name, ldx=128) == qg.QG_ERR_INVALID_ARG       # ldx < K
+    assert call_gemm(name, ldx=260) == qg.QG_ERR_INVALID_ARG       # rows not 16-byte aligned
+    assert call_gemm(name, M=2 ** 31) == qg.QG_ERR_UNSUPPORTED_SHAPE
+
+
+@pytest.mark.parametrize("name", GEMMS)
+def test_gemm_pointer_errors(name):
+    assert call_gemm(name, x=None) == qg.QG_ERR_INVALID_ARG
+    assert call_gemm(name, w=None) == qg.QG_ERR_INVALID_ARG
+    assert call_gemm(name, y=MIS) == qg.QG_ERR_INVALID_ARG
+    assert call_gemm(name, s=MIS) == qg.QG_ERR_INVALID_ARG
+    # an empty batch needs no pointers at all
+    assert call_gemm(name, M=0, x=None, w=None, s=None, y=None) == qg.QG_OK
+
+
+def test_workspace_errors():
+    need = qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 5120, 5120)
+    assert call_gemm("w4a8_gemm", M=64, K=5120, N=5120, ws=None, wsb=0) == qg.QG_ERR_WORKSPACE
+    assert call_gemm("w4a8_gemm", M=64, K=5120, N=5120, ws=FAKE, wsb=need - 1) == qg.QG_ERR_WORKSPACE
+    assert call_gemm("w4a8_gemm", M=64, K=5120, N=5120, ws=MIS, wsb=need) == qg.QG_ERR_INVALID_ARG
+    need16 = qg.qg_workspace_bytes(qg.QG_OP_W4A16, 16, 5120, 5120)
+    assert need16 > 0
+    assert call_gemm("w4a16_gemm", M=16, K=5120, N=5120, ws=FAKE, wsb=need16 - 16) == qg.QG_ERR_WORKSPACE
+
+
+def test_debug_window_errors():
+    f = qg.lib.w4a8_gemm_debug
+    need = qg.qg_workspace_bytes(qg.QG_OP_W4A8, 4, 256, 32)
+    args = [FAKE, 4, 256, 32, 256, FAKE, FAKE, FAKE, FAKE, need, None, None, None, FAKE]
+    assert f(*args, 0, 5, 0, 32) == qg.QG_ERR_INVALID_ARG
+    assert f(*args, 2, 1, 0, 32) == qg.QG_ERR_INVALID_ARG
+    assert f(*args, 0, 4, 0, 33) == qg.QG_ERR_INVALID_ARG
+    assert f(*args, -1, 4, 0, 32) == qg.QG_ERR_INVALID_ARG
+
+
+def test_quantiser_repack_gather_table_errors():
+    L = qg.lib
+    assert L.act_quant_int8(FAKE, 4, 200, 200, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert L.act_quant_int8(FAKE, 4, 256, 128, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.act_quant_int8(None, 4, 256, 256, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.act_quant_int8(None, 0, 256, 256, None, None, None) == qg.QG_OK
+    assert L.w4_repack(FAKE, FAKE, 24, 256, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert L.w4_repack(FAKE, FAKE, 32, 256, None, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.w4_repack(FAKE, FAKE, 0, 256, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.embed_gather_dequant_int8(FAKE, 4, FAKE, FAKE, 10, 100, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert L.embed_gather_dequant_int8(FAKE, -1, FAKE, FAKE, 10, 128, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.embed_gather_dequant_int8(FAKE, 4, FAKE, FAKE, 0, 128, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.embed_gather_dequant_int8(None, 4, FAKE, FAKE, 10, 128, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert L.embed_gather_dequant_int8(None, 0, None, None, 10, 128, None, None) == qg.QG_OK
+    assert L.quant_table_int8(FAKE, 10, 100, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert L.quant_table_int8(FAKE, 10, 128, MIS, FAKE, None) == qg.QG_ERR_INVALID_ARG

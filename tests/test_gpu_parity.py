@@ -1,0 +1,307 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer stages (activation codes, token scales, int32 group partials, the
+gather and the table requantisation) must be bit-exact.  fp16 GEMM outputs
+must satisfy max|y - ref| <= 2^-10 max|ref| and ||y - ref||_F / ||ref||_F
+<= 5e-4 against the float64 oracle (oracle.fp16_bounds).  Full-size
+workloads are compared on every output the oracle can afford and on sampled
+rows / columns otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def qg():
+    import spec_verify_amd
+    return spec_verify_amd
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view({2: np.uint16, 4: np.uint32, 1: np.uint8}[a.dtype.itemsize])
+
+
+def assert_bounds(y, ref, what=""):
+    r = oracle.fp16_bounds(y, ref)
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+def packed(qg, codes, scales):
+    return qg.w4_repack(dev(codes), dev(scales))
+
+
+# ---------------------------------------------------------------------------
+# activation quantiser
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_w4a8", "decode_w4a8", "prefill_w4a8"])
+def test_act_quant_bit_exact_on_workloads(qg, name):
+    cfg = synth.CONFIGS[name]
+    x = synth.acts(cfg["M"], cfg["K"], cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)
+    q, s = qg.act_quant_int8(dev(x))
+    oq, os_ = oracle.quant_act(x)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(bits(host(s)), bits(os_))
+
+
+def test_act_quant_edge_rows_and_strided_input(qg):
+    x = synth.acts(7, 640, 1.0, 0.01, 20.0, seed=9)
+    x[1] = 0                                          # zero row
+    x[2, :6] = [127.0, 0.5, 1.5, 2.5, -2.5, -0.5]     # ties to even with scale 1
+    x[2, 6:] = 0
+    x[3] = np.float16(6e-8)                           # fp16 subnormals
+    x[4] = np.float16(-3.0)                           # constant row
+    wide = np.zeros((7, 648), np.float16)
+    wide[:, :640] = x
+    wide[:, 640:] = np.float16(1000.0)               # past K: must be ignored
+    xd = dev(wide)[:, :640]
+    q, s = qg.act_quant_int8(xd)
+    oq, os_ = oracle.quant_act(x)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(bits(host(s)), bits(os_))
+
+
+def test_act_quant_long_rows_take_the_reload_path(qg):
+    x = synth.acts(3, 40960, 1.0, 0.01, 20.0, seed=10)   # longer than the register-resident chunk count
+    q, s = qg.act_quant_int8(dev(x))
+    oq, os_ = oracle.quant_act(x)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(bits(host(s)), bits(os_))
+    x2 = synth.acts(1100, 20480, 1.0, 0.01, 20.0, seed=12)   # many rows: one wave per row, reloads
+    q2, s2 = qg.act_quant_int8(dev(x2))
+    oq2, os2 = oracle.quant_act(x2)
+    assert np.array_equal(host(q2), oq2)
+    assert np.array_equal(bits(host(s2)), bits(os2))
+
+
+# ---------------------------------------------------------------------------
+# W4A8
+# ---------------------------------------------------------------------------
+
+def _w4a8_check(qg, x, codes, scales, window=None, rows=None):
+    N = codes.shape[0]
+    wp, sp = packed(qg, codes, scales)
+    y, q, s, P = qg.w4a8_gemm_debug(dev(x), wp, sp, N, window=window)
+    oq, os_ = oracle.quant_act(x)
+    assert np.array_equal(host(q), oq), "activation codes"
+    assert np.array_equal(bits(host(s)), bits(os_)), "token scales"
+    m0, m1, n0, n1 = window if window is not None else (0, x.shape[0], 0, N)
+    if m1 > m0 and n1 > n0:
+        assert np.array_equal(host(P).astype(np.int64), oracle.partials(oq[m0:m1], codes[n0:n1])), "int32 partials"
+    yh = host(y)
+    if rows is None:
+        ref = oracle.ref_w4a8(x, codes, scales, q=oq, s=os_)
+        return assert_bounds(yh, ref, "w4a8"), yh
+    ref = oracle.ref_w4a8(x[rows], codes, scales, q=oq[rows], s=os_[rows])
+    return assert_bounds(yh[rows], ref, "w4a8 sampled rows"), yh
+
+
+def test_w4a8_tiny_workload_all_stages(qg):
+    x, codes, scales = synth.gemm_inputs(synth.CONFIGS["tiny_w4a8"])
+    _w4a8_check(qg, x, codes, scales)
+
+
+def test_w4a8_decode_workload_full(qg):
+    cfg = synth.CONFIGS["decode_w4a8"]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    _w4a8_check(qg, x, codes, scales, window=(0, 64, 0, 512))
+    _w4a8_check(qg, x, codes, scales, window=(5, 9, 4600, 5120))
+
+
+@pytest.mark.slow
+def test_w4a8_prefill_workload_sampled(qg):
+    cfg = synth.CONFIGS["prefill_w4a8"]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(4090, 4096),
+                                     rng.choice(4096, 40, replace=False)]))
+    _w4a8_check(qg, x, codes, scales, window=(120, 136, 4990, 5120), rows=rows)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (17, 256, 80), (33, 384, 144), (64, 1024, 48),
+                                   (65, 256, 144), (100, 512, 272), (129, 384, 128), (200, 128, 16)])
+def test_w4a8_ragged_shapes(qg, M, K, N):
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M + K)
+    codes, scales = synth.weights(N, K, seed=N + K)
+    _w4a8_check(qg, x, codes, scales, window=(0, M, 0, N))
+
+
+def test_w4a8_all_minus_8_with_negative_scales_and_zero_rows(qg):
+    """The pages' failure: signed scales read as unsigned.  Every code -8 and
+    every scale negative, plus an all-zero token row."""
+    M, K, N = 5, 256, 32
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=77)
+    x[2] = 0
+    codes = np.full((N, K), -8, np.int8)
+    scales = -np.abs(synth.weights(N, K, seed=78)[1])
+    r, yh = _w4a8_check(qg, x, codes, scales)
+    assert not yh[2].astype(np.float32).any()
+
+
+def test_w4a8_strided_activations(qg):
+    M, K, N = 10, 512, 64
+    wide = synth.acts(M, K + 64, 1.0, 0.01, 20.0, seed=5)
+    x = np.ascontiguousarray(wide[:, :K])
+    codes, scales = synth.weights(N, K, seed=6)
+    wp, sp = packed(qg, codes, scales)
+    y = qg.w4a8_gemm(dev(wide)[:, :K], wp, sp, N)
+    assert_bounds(host(y), oracle.ref_w4a8(x, codes, scales))
+
+
+# ---------------------------------------------------------------------------
+# W4A16
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["verify_w4a16_m8", "verify_w4a16_m16"])
+def test_w4a16_verify_workload_full(qg, name):
+    cfg = synth.CONFIGS[name]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    wp, sp = packed(qg, codes, scales)
+    y = qg.w4a16_gemm(dev(x), wp, sp, cfg["N"])
+    assert_bounds(host(y), oracle.ref_w4a16(x, codes, scales), name)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (8, 5120, 80), (16, 384, 144), (64, 256, 48),
+                                   (65, 256, 32), (150, 384, 96)])
+def test_w4a16_ragged_shapes(qg, M, K, N):
+    x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M * 3 + K)
+    codes, scales = synth.weights(N, K, seed=N * 3 + K)
+    codes[:, :128] = -8
+    wp, sp = packed(qg, codes, scales)
+    y = qg.w4a16_gemm(dev(x), wp, sp, N)
+    assert_bounds(host(y), oracle.ref_w4a16(x, codes, scales))
+
+
+# ---------------------------------------------------------------------------
+# int8 vocabulary table: requantisation, gather, lm_head
+# ---------------------------------------------------------------------------
+
+def test_quant_table_bit_exact(qg):
+    src = synth.table_source(3000, 640, seed=21)
+    src[7, :128] = 0
+    Q, S = qg.quant_table_int8(dev(src.view(np.int16)))
+    oQ, oS = oracle.quant_table(src)
+    assert np.array_equal(host(Q), oQ)
+    assert np.array_equal(bits(host(S)), bits(oS))
+
+
+def test_gather_bit_exact_with_out_of_range_ids(qg):
+    src = synth.table_source(1000, 384, seed=22)
+    oQ, oS = oracle.quant_table(src)
+    ids = np.array([0, 999, -1, 1000, 5, 5, 2 ** 31 - 1, 123], np.int32)
+    out = qg.embed_gather_dequant_int8(dev(ids), dev(oQ), dev(oS))
+    assert np.array_equal(bits(host(out)), bits(oracle.ref_gather(ids, oQ, oS)))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (64, 640, 400), (8, 256, 1040), (70, 256, 64)])
+def test_w8a16_ragged_shapes(qg, M, K, N):
+    src = synth.table_source(N, K, seed=N + 1)
+    Q, S = oracle.quant_table(src)
+    x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M + 2)
+    y = qg.w8a16_gemm(dev(x), dev(Q), dev(S))
+    assert_bounds(host(y), oracle.ref_w8a16(x, Q, S))
+
+
+@pytest.mark.slow
+def test_vocab_workload_full_table(qg):
+    """248,320 x 5,120 table: requantised on the device, then the 64-id
+    gather (bit-exact) and the M=64 lm_head (sampled columns)."""
+    cfg = synth.CONFIGS["vocab_int8"]
+    V, H, seed = cfg["V"], cfg["H"], cfg["seed"]
+    src = synth.table_source(V, H, seed + 200)
+    Qd, Sd = qg.quant_table_int8(dev(src.view(np.int16)))
+    rng = np.random.default_rng(1)
+    check_rows = np.unique(np.concatenate([rng.choice(V, 2048, replace=False), [0, V - 1]]))
+    oQ, oS = oracle.quant_table(src[check_rows])
+    assert np.array_equal(host(Qd[torch.from_numpy(check_rows).to(DEV)]), oQ)
+    assert np.array_equal(bits(host(Sd[torch.from_numpy(check_rows).to(DEV)])), bits(oS))
+
+    ids = synth.token_ids(cfg["T"], V, seed + 300)
+    out = qg.embed_gather_dequant_int8(dev(ids), Qd, Sd)
+    gQ, gS = oracle.quant_table(src[ids])
+    want = oracle.ref_gather(np.arange(len(ids), dtype=np.int32), gQ, gS)
+    assert np.array_equal(bits(host(out)), bits(want))
+
+    x = synth.acts(cfg["M"], H, cfg["sigma"], cfg["p"], cfg["factor"], seed + 100)
+    y = qg.w8a16_gemm(dev(x), Qd, Sd)
+    cols = np.unique(np.concatenate([rng.choice(V, 4096, replace=False), np.arange(V - 16, V)]))
+    cQ, cS = oracle.quant_table(src[cols])
+    assert_bounds(host(y)[:, cols], oracle.ref_w8a16(x, cQ, cS), "lm_head sampled columns")
+    del Qd, Sd, src
+
+
+# ---------------------------------------------------------------------------
+# properties: empty input, batch invariance, determinism, no stray writes
+# ---------------------------------------------------------------------------
+
+def test_empty_batch_is_a_no_op(qg):
+    codes, scales = synth.weights(32, 256, seed=1)
+    wp, sp = packed(qg, codes, scales)
+    x = torch.empty((0, 256), dtype=torch.float16, device=DEV)
+    for fn in (qg.w4a8_gemm, qg.w4a16_gemm):
+        y = fn(x, wp, sp, 32)
+        assert y.shape == (0, 32)
+    out = qg.embed_gather_dequant_int8(torch.empty((0,), dtype=torch.int32, device=DEV),
+                                       dev(np.zeros((4, 128), np.int8)), dev(np.zeros((4, 1), np.float16)))
+    assert out.shape == (0, 128)
+
+
+@pytest.mark.parametrize("op", ["w4a8", "w4a16"])
+def test_rows_do_not_depend_on_the_batch(qg, op):
+    """A token's output does not change with the other tokens in the batch
+    (M = 1, 8, 16, 64 all take the weight-streaming kernel): bit-identical."""
+    cfg = synth.CONFIGS["decode_w4a8"]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    wp, sp = packed(qg, codes, scales)
+    fn = qg.w4a8_gemm if op == "w4a8" else qg.w4a16_gemm
+    full = host(fn(dev(x), wp, sp, cfg["N"]))
+    for M in (1, 8, 16):
+        part = host(fn(dev(x[:M]), wp, sp, cfg["N"]))
+        assert np.array_equal(bits(part), bits(full[:M])), M
+
+
+@pytest.mark.parametrize("name", ["decode_w4a8", "verify_w4a16_m16"])
+def test_repeat_runs_are_bit_identical(qg, name):
+    cfg = synth.CONFIGS[name]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    wp, sp = packed(qg, codes, scales)
+    fn = qg.w4a8_gemm if cfg["op"] == "w4a8" else qg.w4a16_gemm
+    xd = dev(x)
+    a = host(fn(xd, wp, sp, cfg["N"]))
+    b = host(fn(xd, wp, sp, cfg["N"]))
+    assert np.array_equal(bits(a), bits(b))
+
+
+@pytest.mark.parametrize("M,N", [(3, 48), (64, 80), (130, 144)])
+def test_outputs_stay_inside_their_buffer(qg, M, N):
+    """Canary-filled padding around y is untouched after the call."""
+    K = 256
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=3)
+    codes, scales = synth.weights(N, K, seed=4)
+    wp, sp = packed(qg, codes, scales)
+    pad = 4096
+    for fn in (qg.w4a8_gemm, qg.w4a16_gemm):
+        buf = torch.full((M * N + 2 * pad,), 0x7bcd, dtype=torch.int16, device=DEV)
+        y = buf[pad:pad + M * N].view(torch.float16).view(M, N)
+        fn(dev(x), wp, sp, N, y=y)
+        hb = host(buf)
+        assert (hb[:pad] == 0x7bcd).all() and (hb[pad + M * N:] == 0x7bcd).all()
