@@ -1,0 +1,238 @@
+"""Throughput of the weight-only-int4 GEMM path on one MI355X.
+
+A step is one W4A8 call on the decode-batch workload (M = 64 tokens, one per
+concurrent sequence; K = N = 5120; int4 group-128 weights with signed fp16
+scales): per-token int8 quantisation of the activations, then the int8
+matrix-core GEMM with per-group rescale.  Inputs are seeded synthetic tensors
+already resident in HBM.  The weights rotate over enough packed copies that
+every call reads a copy not touched for > 512 MB of traffic, so the 256 MB
+Infinity Cache cannot serve repeats.  Steps are captured in a HIP graph and
+replayed; the timed region is bracketed by device synchronisation.
+
+Printed: one JSON line.  `value` is algorithmic HBM bytes per step (weights,
+scales, fp16 activations, fp16 output, each counted once) per second.
+`roofline` is the dominant kernel (the GEMM, timed alone via
+w4a8_gemm_prepared) against the 8 TB/s HBM peak.  `cpu_baseline` is the
+numpy oracle on the same workload on the host's cores.  `per_workload` adds
+the verify (W4A16, M = 8/16, N = 34816), prefill (W4A8, M = 4096, K = 17408)
+and vocabulary (int8 gather + lm_head over 248,320 rows) workloads measured
+the same way, for information.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A8/W4A16 GEMM TOPS + HBM GB/s (% roofline) at M=8/64/4096, K=N=5120"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+FP16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-workload extras")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def gemm_bytes(M, K, N):
+    """Algorithmic HBM bytes of one W4A*/W4A16 GEMM call: packed int4 weights,
+    fp16 group scales, fp16 activations, fp16 output."""
+    return N * K // 2 + N * (K // 128) * 2 + M * K * 2 + M * N * 2
+
+
+def copies_for(nbytes):
+    return max(2, -(-2 * MALL_BYTES // nbytes) + 1)
+
+
+def graph_time_us(torch, fn, n_calls, reps=1):
+    """Capture n_calls of fn(i) in a graph, replay `reps` times, return
+    microseconds per call (HIP events on the replay stream)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (n_calls * reps), g
+
+
+def cpu_baseline(x, codes, scales, seconds):
+    """The numpy oracle (quantise, exact group partials, float64 rescale) on the
+    decode workload, repeated for about `seconds` on the host's cores."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    M, K = x.shape
+    N = codes.shape[0]
+    with threadpool_limits(limits=os.cpu_count() or 1):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        oracle.ref_w4a8(x, codes, scales)     # warm up
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.ref_w4a8(x, codes, scales)
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                break
+    per_call = dt / n
+    return dict(value=round(gemm_bytes(M, K, N) / per_call / 1e9, 3), unit="GB/s", cores=int(threads),
+                kind="oracle", seconds_per_call=round(per_call, 5),
+                sample=f"{n} full oracle evaluations of the decode workload (M=64, K=N=5120) in {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the path is single-GPU and no multi-GPU run is defined "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import spec_verify_amd as qg
+    import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS["decode_w4a8"]
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    xd = torch.from_numpy(x).to(dev)
+    wp, sp = qg.w4_repack(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    ncopy = copies_for(wp.numel() + sp.numel() * 2)
+    copies = [(wp.clone(), sp.clone()) for _ in range(ncopy)]
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws = torch.empty((qg.qg_workspace_bytes(qg.QG_OP_W4A8, M, K, N),), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        w, s = copies[i % ncopy]
+        qg.w4a8_gemm(xd, w, s, N, y=y, workspace=ws)
+
+    # warmup graph, then the timed graph of exactly `steps` calls
+    graph_time_us(torch, step, max(1, args.warmup))
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(args.steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+    step_bytes = gemm_bytes(M, K, N)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: the GEMM alone on prepared (quantised) activations
+    prep = qg.w4a8_prepare(xd)
+    torch.cuda.synchronize()
+    gemm_us, _ = graph_time_us(
+        torch, lambda i: qg.w4a8_gemm_prepared(prep, M, K, copies[i % ncopy][0], copies[i % ncopy][1], N, y=y),
+        max(ncopy, 200))
+    kernel_bytes = N * K // 2 + N * (K // 128) * 2 + M * K + M * 4 + M * N * 2
+    achieved = kernel_bytes / (gemm_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", kernel="skinny_kernel<W4A8> (w4a8_gemm_prepared)", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                    bytes_per_launch=kernel_bytes, avg_launch_us=round(gemm_us, 3), traffic=None)
+
+    out = dict(metric=METRIC, value=round(value, 2), unit="GB/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms_per_step, 6), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="int8", data="synthetic",
+               config=dict(workload="decode_w4a8: W4A8 GEMM, M=64 tokens, K=5120, N=5120, int4 group-128 "
+                                    "weights with signed fp16 scales, fp16 activations N(0,1) with 1% x20 "
+                                    "outliers, quantised per token inside the call, fp16 output",
+                           M=M, K=K, N=N, weight_copies=ncopy, graph_replay=True),
+               tops=round(2 * M * N * K / (ms_per_step * 1e-3) / 1e12, 3),
+               frac_hbm=round(value / HBM_PEAK_GBS, 4), wall_s=round(wall, 4), roofline=roofline)
+
+    if not args.no_extra:
+        out["per_workload"] = extras(torch, qg, synth, np, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, codes, scales, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def extras(torch, qg, synth, np, dev):
+    res = {}
+    for name in ("verify_w4a16_m8", "verify_w4a16_m16", "prefill_w4a8"):
+        cfg = synth.CONFIGS[name]
+        M, K, N = cfg["M"], cfg["K"], cfg["N"]
+        x, codes, scales = synth.gemm_inputs(cfg)
+        xd = torch.from_numpy(x).to(dev)
+        wp, sp = qg.w4_repack(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+        ncopy = copies_for(wp.numel() + sp.numel() * 2)
+        copies = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(ncopy - 1)]
+        y = torch.empty((M, N), dtype=torch.float16, device=dev)
+        if cfg["op"] == "w4a8":
+            ws = torch.empty((qg.qg_workspace_bytes(qg.QG_OP_W4A8, M, K, N),), dtype=torch.uint8, device=dev)
+            fn = lambda i: qg.w4a8_gemm(xd, copies[i % ncopy][0], copies[i % ncopy][1], N, y=y, workspace=ws)
+        else:
+            fn = lambda i: qg.w4a16_gemm(xd, copies[i % ncopy][0], copies[i % ncopy][1], N, y=y)
+        us, _ = graph_time_us(torch, fn, 4 * ncopy if M <= 64 else ncopy, reps=2)
+        b = gemm_bytes(M, K, N)
+        ops = 2 * M * N * K
+        peak_ops = INT8_PEAK_TOPS if cfg["op"] == "w4a8" else FP16_PEAK_TFLOPS
+        res[name] = dict(M=M, K=K, N=N, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
+                         frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), TOPS=round(ops / us / 1e6, 2),
+                         frac_mfma=round(ops / us / 1e6 / peak_ops, 4), weight_copies=ncopy)
+        del copies, wp, sp
+        torch.cuda.empty_cache()
+
+    cfg = synth.CONFIGS["vocab_int8"]
+    V, H = cfg["V"], cfg["H"]
+    src = torch.from_numpy(synth.table_source(V, H, cfg["seed"] + 200).view(np.int16)).to(dev)
+    Q, S = qg.quant_table_int8(src)
+    del src
+    ids = torch.from_numpy(synth.token_ids(cfg["T"], V, cfg["seed"] + 300)).to(dev)
+    out = torch.empty((cfg["T"], H), dtype=torch.float16, device=dev)
+    us, _ = graph_time_us(torch, lambda i: qg.embed_gather_dequant_int8(ids, Q, S, out=out), 200)
+    res["vocab_gather_t64"] = dict(T=cfg["T"], H=H, us_per_call=round(us, 3),
+                                   bytes=cfg["T"] * (H + H // 128 * 2 + H * 2))
+    x = torch.from_numpy(synth.acts(cfg["M"], H, cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)).to(dev)
+    y = torch.empty((cfg["M"], V), dtype=torch.float16, device=dev)
+    us, _ = graph_time_us(torch, lambda i: qg.w8a16_gemm(x, Q, S, y=y), 10, reps=2)
+    b = V * H + V * (H // 128) * 2 + cfg["M"] * H * 2 + cfg["M"] * V * 2
+    res["lm_head_w8a16_m64"] = dict(M=cfg["M"], K=H, N=V, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
+                                    frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                                    TFLOPS=round(2 * cfg["M"] * V * H / us / 1e6, 2))
+    return res
+
+
+if __name__ == "__main__":
+    main()

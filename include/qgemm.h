@@ -68,9 +68,9 @@ size_t w4_packed_bytes(int64_t N, int64_t K);
 size_t w4_scales_bytes(int64_t N, int64_t K);
 
 /* Bytes of device workspace the GEMM `op` needs for this shape (0 is a valid
- * answer: no workspace needed).  Returns (size_t)-1 for an invalid op or
- * shape.  The workspace holds the int8 activation codes and token scales of
- * W4A8 and the fp32 split-K partial sums; it needs no initialisation and its
+ * answer: no workspace needed, as for w4a16_gemm and w8a16_gemm).  Returns
+ * (size_t)-1 for an invalid op or shape.  The W4A8 workspace holds the int8
+ * activation codes and the token scales; it needs no initialisation and its
  * contents after a call are unspecified. */
 size_t qg_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
 
@@ -109,8 +109,7 @@ int w4_repack(const int8_t* codes, const void* scales_f16, int64_t N, int64_t K,
  *   y         fp16 [M][N] out: y[m][n] = fp16(sum_k x[m][k] * codes[n][k] * scales[n][k/128]),
  *             products of fp16 x and exact int4 codes accumulated in fp32,
  *             each 128-wide group rescaled by its fp32 scale.
- *   workspace  >= qg_workspace_bytes(QG_OP_W4A16, M, K, N) bytes (may be
- *             NULL when that is 0)
+ *   workspace, ws_bytes  unused (qg_workspace_bytes gives 0); may be NULL, 0
  */
 int w4a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
                const void* w_packed, const void* s_packed, void* y_f16,
@@ -129,6 +128,27 @@ int w4a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
 int w4a8_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
               const void* w_packed, const void* s_packed, void* y_f16,
               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * w4a8_prepare / w4a8_gemm_prepared -- w4a8_gemm in two steps, so one
+ * quantised activation can feed several GEMMs (for example the fused
+ * gate/up projection and the q/k/v projections of the same hidden state).
+ *   w4a8_prepared_bytes(M, K)  size of the opaque prepared buffer ((size_t)-1
+ *                              for an unsupported shape, 0 for M == 0)
+ *   w4a8_prepare   quantises x per token (exactly as act_quant_int8) into
+ *                  `prepared` (prepared_bytes >= w4a8_prepared_bytes(M, K)),
+ *                  codes in the order the GEMM for this M reads, plus the
+ *                  fp32 token scales.  The buffer is only meaningful to
+ *                  w4a8_gemm_prepared with the same M and K.
+ *   w4a8_gemm_prepared  y = the W4A8 product of that quantised x with the
+ *                  packed weights; bit-identical to w4a8_gemm on the same x.
+ *                  Launches exactly one kernel.
+ */
+size_t w4a8_prepared_bytes(int64_t M, int64_t K);
+int w4a8_prepare(const void* x_f16, int64_t M, int64_t K, int64_t ldx, void* prepared, size_t prepared_bytes,
+                 void* stream);
+int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, const void* w_packed,
+                       const void* s_packed, void* y_f16, void* stream);
 
 /*
  * w4a8_gemm_debug -- w4a8_gemm that also exposes its integer stages, for

@@ -7,7 +7,8 @@ torch stream.  All arithmetic runs in the library's HIP kernels.  If the
 library has not been built the import fails; there is no fallback.
 
 Entry points (see ``include/qgemm.h`` for the contract of each):
-act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_gemm_debug,
+act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare,
+w4a8_gemm_prepared, w4a8_gemm_debug,
 w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, plus the size
 helpers w4_packed_bytes, w4_scales_bytes, qg_workspace_bytes and
 qg_status_string.
@@ -49,6 +50,9 @@ _SIGS = {
     "w4_repack": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _p]),
     "w4a16_gemm": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "w4a8_gemm": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
+    "w4a8_prepared_bytes": (_sz, [_i64, _i64]),
+    "w4a8_prepare": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _sz, _p]),
+    "w4a8_gemm_prepared": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "w4a8_gemm_debug": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p,
                                        _p, _p, _p, _i64, _i64, _i64, _i64]),
     "w8a16_gemm": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
@@ -161,6 +165,31 @@ def w4a8_gemm(x, w_packed, s_packed, N, y=None, workspace=None):
     ws, wsz = _workspace(QG_OP_W4A8, M, K, N, x, workspace)
     _check("w4a8_gemm", lib.w4a8_gemm(_ptr(x), M, K, N, _ldx(x), _ptr(w_packed), _ptr(s_packed), _ptr(y),
                                       _ptr(ws), wsz, _stream(x.device)))
+    return y
+
+
+def w4a8_prepared_bytes(M: int, K: int) -> int:
+    return int(lib.w4a8_prepared_bytes(M, K))
+
+
+def w4a8_prepare(x, prepared=None):
+    """Quantise x [M, K] per token into an opaque prepared buffer (uint8) for
+    w4a8_gemm_prepared."""
+    import torch
+    M, K = x.shape
+    need = w4a8_prepared_bytes(M, K)
+    prepared = _empty((max(1, need),), torch.uint8, x) if prepared is None else prepared
+    _check("w4a8_prepare", lib.w4a8_prepare(_ptr(x), M, K, _ldx(x), _ptr(prepared),
+                                            prepared.numel() * prepared.element_size(), _stream(x.device)))
+    return prepared
+
+
+def w4a8_gemm_prepared(prepared, M, K, w_packed, s_packed, N, y=None):
+    """fp16 y [M, N] from a buffer made by w4a8_prepare (one kernel launch)."""
+    import torch
+    y = _empty((M, N), torch.float16, prepared) if y is None else y
+    _check("w4a8_gemm_prepared", lib.w4a8_gemm_prepared(_ptr(prepared), M, K, N, _ptr(w_packed), _ptr(s_packed),
+                                                        _ptr(y), _stream(prepared.device)))
     return y
 
 

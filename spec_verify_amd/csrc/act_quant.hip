@@ -7,9 +7,17 @@
 //
 // HBM-bound (2 bytes in, 1 byte out per element).  A row is held in registers
 // between the absmax pass and the quantise pass, so x is read from HBM once.
-// Small batches (the decode regime) spread one row over a 256-thread
-// workgroup to keep enough loads in flight; large batches give each row one
-// wavefront so the absmax needs no barrier.
+// One 256-thread workgroup per row; rows longer than the register budget are
+// re-read (from cache) in the quantise pass.
+//
+// Output orders.  Row-major q[m][k], and/or the "fragment" order the
+// weight-streaming W4A8 GEMM loads: rows in tiles of 16, and for tile mt,
+// group g, half h (64 k) a 1 KiB block at byte ((mt*G + g)*2 + h) * 1024 in
+// which lane l = col + 16*quad owns the 16 codes of row 16*mt + col at
+// k = 128 g + 64 h + 16 quad + [0, 16).  That is exactly one 16-byte operand
+// of v_mfma_i32_16x16x64_i8 per lane, so the GEMM moves it with one
+// contiguous 1 KiB load.  Rows of the last tile past M are left unwritten
+// (the GEMM never stores their results).
 #include "common.h"
 
 namespace qg {
@@ -50,7 +58,8 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s) {
 template <int THREADS, int MAXC>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                         int K, int64_t M, int8_t* __restrict__ q,
-                                                        int64_t ldq, float* __restrict__ scale) {
+                                                        int64_t ldq, int8_t* __restrict__ qfrag,
+                                                        float* __restrict__ scale) {
   constexpr int ROWS = 256 / THREADS;
   const int t = threadIdx.x % THREADS;
   const int64_t m = (int64_t)blockIdx.x * ROWS + threadIdx.x / THREADS;
@@ -85,39 +94,41 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 
   const float s = a / 127.0f;   // IEEE fp32 division
   if (t == 0) scale[m] = a > 0.0f ? s : 0.0f;
-  int8_t* qrow = q + m * ldq;
+  const int G = K / kGroup;
+  const int mt = (int)(m >> 4), col = (int)(m & 15);
+  // stores the 8 codes of chunk c (k = 8c .. 8c+7) in the requested orders
+  auto put = [&](int c, uint2 codes) {
+    if (q) *reinterpret_cast<uint2*>(q + m * ldq + 8 * c) = codes;
+    if (qfrag) {
+      const int k = 8 * c, g = k >> 7, kk = k & 127, h = kk >> 6, quad = (kk & 63) >> 4;
+      const int64_t off = ((((int64_t)mt * G + g) * 2 + h) * 64 + col + 16 * quad) * 16 + (kk & 15);
+      *reinterpret_cast<uint2*>(qfrag + off) = codes;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int c = t + THREADS * i;
-    if (c < nch)
-      *reinterpret_cast<uint2*>(qrow + 8 * c) = a > 0.0f ? quant8(v[i], s) : make_uint2(0, 0);
+    if (c < nch) put(c, a > 0.0f ? quant8(v[i], s) : make_uint2(0, 0));
   }
   for (int c = t + THREADS * MAXC; c < nch; c += THREADS)
-    *reinterpret_cast<uint2*>(qrow + 8 * c) =
-        a > 0.0f ? quant8(*reinterpret_cast<const uint4*>(row + 8 * c), s) : make_uint2(0, 0);
+    put(c, a > 0.0f ? quant8(*reinterpret_cast<const uint4*>(row + 8 * c), s) : make_uint2(0, 0));
 }
 
 }  // namespace
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
-                            int64_t ldq, float* scale, hipStream_t st) {
+                            int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const int nch = (int)(K / 8);
-  if (M < 1024) {
-    // decode-sized batches: one 256-thread workgroup per row
-    dim3 grid((unsigned)M);
-    if (nch <= 256 * 4)
-      act_quant_kernel<256, 4><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, scale);
-    else
-      act_quant_kernel<256, 12><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, scale);
-  } else {
-    // prefill-sized batches: one wavefront per row, four rows per workgroup
-    dim3 grid((unsigned)((M + 3) / 4));
-    if (nch <= 64 * 12)
-      act_quant_kernel<64, 12><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, scale);
-    else
-      act_quant_kernel<64, 36><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, scale);
-  }
+  // One 256-thread workgroup per row: a few 16-byte chunks per thread keep
+  // many rows' loads in flight and the divides spread over more waves.
+  const dim3 grid((unsigned)M);
+  if (nch <= 256 * 4)
+    act_quant_kernel<256, 4><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, qfrag, scale);
+  else if (nch <= 256 * 12)
+    act_quant_kernel<256, 12><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, qfrag, scale);
+  else
+    act_quant_kernel<256, 24><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, qfrag, scale);
   return hipGetLastError();
 }
 

@@ -48,33 +48,21 @@ int check_ptrs(int64_t M, const void* x, const void* w, const void* s, const voi
   return QG_OK;
 }
 
-// Workspace layout of w4a8_gemm: int8 codes [M][K], fp32 token scales [M],
-// then fp32 split-K partial sums [splits][M][N] for the weight-streaming
-// kernel.  Each region starts on a 256-byte boundary.
+// Workspace layout of w4a8_gemm: the int8 activation codes (fragment order
+// in tiles of 16 rows for the weight-streaming kernel, M <= 64; row-major
+// [M][K] for the tiled kernel), then the fp32 token scales [M], each on a
+// 256-byte boundary.
 struct W4A8Layout {
-  size_t q_off, s_off, p_off, total;
+  size_t q_off, s_off, total;
 };
 
-W4A8Layout w4a8_layout(int64_t M, int64_t K, int64_t N) {
+W4A8Layout w4a8_layout(int64_t M, int64_t K) {
   W4A8Layout L;
+  const int64_t rows = M <= kSkinnyMaxM ? (M + 15) / 16 * 16 : M;
   L.q_off = 0;
-  L.s_off = round_up((size_t)M * (size_t)K, 256);
-  L.p_off = round_up(L.s_off + (size_t)M * 4, 256);
-  size_t part = 0;
-  if (M <= kSkinnyMaxM) {
-    const int s = qg::skinny_splits(N, K);
-    if (s > 1) part = (size_t)s * (size_t)M * (size_t)N * 4;
-  }
-  L.total = L.p_off + part;
+  L.s_off = round_up((size_t)rows * (size_t)K, 256);
+  L.total = L.s_off + (size_t)M * 4;
   return L;
-}
-
-// Partial-sum bytes of w4a16_gemm / w8a16_gemm (they run M in chunks of 64).
-size_t streaming_partials_bytes(int64_t M, int64_t K, int64_t N) {
-  const int s = qg::skinny_splits(N, K);
-  if (s <= 1 || M == 0) return 0;
-  const int64_t mc = M < kSkinnyMaxM ? M : kSkinnyMaxM;
-  return (size_t)s * (size_t)mc * (size_t)N * 4;
 }
 
 int gemm_streaming(int mode, const void* x, int64_t M, int64_t K, int64_t N, int64_t ldx,
@@ -83,9 +71,8 @@ int gemm_streaming(int mode, const void* x, int64_t M, int64_t K, int64_t N, int
   if (st != QG_OK) return st;
   if ((st = check_ptrs(M, x, w, s, y)) != QG_OK) return st;
   if (M == 0) return QG_OK;
-  const size_t need = streaming_partials_bytes(M, K, N);
-  if (need > 0 && (!ws || ws_bytes < need)) return QG_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(ws)) return QG_ERR_INVALID_ARG;
+  (void)ws;
+  (void)ws_bytes;
   clear_stale_error();
   for (int64_t m0 = 0; m0 < M; m0 += kSkinnyMaxM) {
     qg::SkinnyArgs a = {};
@@ -99,12 +86,66 @@ int gemm_streaming(int mode, const void* x, int64_t M, int64_t K, int64_t N, int
     a.N = N;
     a.K = K;
     a.y = reinterpret_cast<uint16_t*>(y) + m0 * N;
-    a.partials = reinterpret_cast<float*>(ws);
     a.dbg = nullptr;
     st = launch_status(qg::launch_skinny(a, as_stream(stream)));
     if (st != QG_OK) return st;
   }
   return QG_OK;
+}
+
+int check_w4a8_shape(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K <= 0 || N <= 0) return QG_ERR_INVALID_ARG;
+  if (K % kGroup != 0 || N % 16 != 0) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  return QG_OK;
+}
+
+// Quantise x into a prepared buffer (codes in the order the GEMM for this M
+// reads, then the token scales).  q_row: optional extra row-major copy.
+int prepare_impl(const void* x, int64_t M, int64_t K, int64_t ldx, void* prepared, int8_t* q_row,
+                 hipStream_t hs) {
+  const W4A8Layout L = w4a8_layout(M, K);
+  char* base = reinterpret_cast<char*>(prepared);
+  int8_t* q = reinterpret_cast<int8_t*>(base + L.q_off);
+  float* ts = reinterpret_cast<float*>(base + L.s_off);
+  const bool skinny = M <= kSkinnyMaxM;
+  // Codes: fragment order for the weight-streaming kernel, row-major for the
+  // tiled one; the optional extra copy is always row-major.
+  return launch_status(qg::launch_act_quant(reinterpret_cast<const uint16_t*>(x), M, K, ldx,
+                                            skinny ? q_row : q, K, skinny ? q : nullptr, ts, hs));
+}
+
+int gemm_prepared_impl(const void* prepared, int64_t M, int64_t K, int64_t N, const void* w_packed,
+                       const void* s_packed, void* y, hipStream_t hs, int32_t* dbg, int64_t m0, int64_t m1,
+                       int64_t n0, int64_t n1) {
+  const W4A8Layout L = w4a8_layout(M, K);
+  const char* base = reinterpret_cast<const char*>(prepared);
+  const int8_t* q = reinterpret_cast<const int8_t*>(base + L.q_off);
+  const float* ts = reinterpret_cast<const float*>(base + L.s_off);
+  if (M <= kSkinnyMaxM) {
+    qg::SkinnyArgs a = {};
+    a.mode = qg::kW4A8;
+    a.act = q;
+    a.lda = K;
+    a.tok_scale = ts;
+    a.w = w_packed;
+    a.s = reinterpret_cast<const uint16_t*>(s_packed);
+    a.M = M; a.N = N; a.K = K;
+    a.y = reinterpret_cast<uint16_t*>(y);
+    a.dbg = dbg;
+    a.dm0 = m0; a.dm1 = m1; a.dn0 = n0; a.dn1 = n1;
+    return launch_status(qg::launch_skinny(a, hs));
+  }
+  qg::LargeArgs a = {};
+  a.codes = q;
+  a.tok_scale = ts;
+  a.w = w_packed;
+  a.s = reinterpret_cast<const uint16_t*>(s_packed);
+  a.M = M; a.N = N; a.K = K;
+  a.y = reinterpret_cast<uint16_t*>(y);
+  a.dbg = dbg;
+  a.dm0 = m0; a.dm1 = m1; a.dn0 = n0; a.dn1 = n1;
+  return launch_status(qg::launch_w4a8_large(a, hs));
 }
 
 int w4a8_impl(const void* x, int64_t M, int64_t K, int64_t N, int64_t ldx, const void* w_packed,
@@ -116,53 +157,27 @@ int w4a8_impl(const void* x, int64_t M, int64_t K, int64_t N, int64_t ldx, const
   if (partials && !(0 <= m0 && m0 <= m1 && m1 <= M && 0 <= n0 && n0 <= n1 && n1 <= N))
     return QG_ERR_INVALID_ARG;
   if (M == 0) return QG_OK;
-  const W4A8Layout L = w4a8_layout(M, K, N);
+  const W4A8Layout L = w4a8_layout(M, K);
   if (!ws || ws_bytes < L.total) return QG_ERR_WORKSPACE;
   if (!aligned16(ws)) return QG_ERR_INVALID_ARG;
   if ((q_out && !aligned16(q_out)) || (partials && (reinterpret_cast<uintptr_t>(partials) & 3u)) ||
       (scale_out && (reinterpret_cast<uintptr_t>(scale_out) & 3u)))
     return QG_ERR_INVALID_ARG;
-
-  char* base = reinterpret_cast<char*>(ws);
-  int8_t* q = reinterpret_cast<int8_t*>(base + L.q_off);
-  float* ts = reinterpret_cast<float*>(base + L.s_off);
   hipStream_t hs = as_stream(stream);
   int32_t* dbg = (partials && m1 > m0 && n1 > n0) ? partials : nullptr;
+  const bool skinny = M <= kSkinnyMaxM;
 
   clear_stale_error();
-  st = launch_status(qg::launch_act_quant(reinterpret_cast<const uint16_t*>(x), M, K, ldx, q, K, ts, hs));
+  st = prepare_impl(x, M, K, ldx, ws, skinny ? q_out : nullptr, hs);
   if (st != QG_OK) return st;
-  if (M <= kSkinnyMaxM) {
-    qg::SkinnyArgs a = {};
-    a.mode = qg::kW4A8;
-    a.act = q;
-    a.lda = K;
-    a.tok_scale = ts;
-    a.w = w_packed;
-    a.s = reinterpret_cast<const uint16_t*>(s_packed);
-    a.M = M; a.N = N; a.K = K;
-    a.y = reinterpret_cast<uint16_t*>(y);
-    a.partials = reinterpret_cast<float*>(base + L.p_off);
-    a.dbg = dbg;
-    a.dm0 = m0; a.dm1 = m1; a.dn0 = n0; a.dn1 = n1;
-    st = launch_status(qg::launch_skinny(a, hs));
-  } else {
-    qg::LargeArgs a = {};
-    a.codes = q;
-    a.tok_scale = ts;
-    a.w = w_packed;
-    a.s = reinterpret_cast<const uint16_t*>(s_packed);
-    a.M = M; a.N = N; a.K = K;
-    a.y = reinterpret_cast<uint16_t*>(y);
-    a.dbg = dbg;
-    a.dm0 = m0; a.dm1 = m1; a.dn0 = n0; a.dn1 = n1;
-    st = launch_status(qg::launch_w4a8_large(a, hs));
-  }
+  st = gemm_prepared_impl(ws, M, K, N, w_packed, s_packed, y, hs, dbg, m0, m1, n0, n1);
   if (st != QG_OK) return st;
-  if (q_out && (st = launch_status(hipMemcpyAsync(q_out, q, (size_t)M * K, hipMemcpyDeviceToDevice, hs))) != QG_OK)
+  const char* base = reinterpret_cast<const char*>(ws);
+  if (!skinny && q_out &&
+      (st = launch_status(hipMemcpyAsync(q_out, base + L.q_off, (size_t)M * K, hipMemcpyDeviceToDevice, hs))) != QG_OK)
     return st;
   if (scale_out &&
-      (st = launch_status(hipMemcpyAsync(scale_out, ts, (size_t)M * 4, hipMemcpyDeviceToDevice, hs))) != QG_OK)
+      (st = launch_status(hipMemcpyAsync(scale_out, base + L.s_off, (size_t)M * 4, hipMemcpyDeviceToDevice, hs))) != QG_OK)
     return st;
   return QG_OK;
 }
@@ -199,9 +214,9 @@ size_t w4_scales_bytes(int64_t N, int64_t K) {
 size_t qg_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
   if (check_gemm_shape(M, K, N, K + (8 - K % 8) % 8) != QG_OK) return (size_t)-1;
   switch (op) {
-    case QG_OP_W4A8: return M == 0 ? 0 : w4a8_layout(M, K, N).total;
+    case QG_OP_W4A8: return M == 0 ? 0 : w4a8_layout(M, K).total;
     case QG_OP_W4A16:
-    case QG_OP_W8A16: return streaming_partials_bytes(M, K, N);
+    case QG_OP_W8A16: return 0;
     default: return (size_t)-1;
   }
 }
@@ -216,7 +231,7 @@ int act_quant_int8(const void* x_f16, int64_t M, int64_t K, int64_t ldx, int8_t*
     return QG_ERR_INVALID_ARG;
   clear_stale_error();
   return launch_status(qg::launch_act_quant(reinterpret_cast<const uint16_t*>(x_f16), M, K, ldx, q, K,
-                                            scale, as_stream(stream)));
+                                            nullptr, scale, as_stream(stream)));
 }
 
 int w4_repack(const int8_t* codes, const void* scales_f16, int64_t N, int64_t K, void* w_packed,
@@ -250,6 +265,33 @@ int w4a8_gemm_debug(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t 
                     int64_t n1) {
   return w4a8_impl(x_f16, M, K, N, ldx, w_packed, s_packed, y_f16, workspace, ws_bytes, stream, q_out,
                    scale_out, partials, m0, m1, n0, n1);
+}
+
+size_t w4a8_prepared_bytes(int64_t M, int64_t K) {
+  if (check_w4a8_shape(M, K, 16) != QG_OK) return (size_t)-1;
+  return M == 0 ? 0 : w4a8_layout(M, K).total;
+}
+
+int w4a8_prepare(const void* x_f16, int64_t M, int64_t K, int64_t ldx, void* prepared, size_t prepared_bytes,
+                 void* stream) {
+  int st = check_w4a8_shape(M, K, 16);
+  if (st != QG_OK) return st;
+  if (ldx < K || ldx % 8 != 0) return QG_ERR_INVALID_ARG;
+  if (M == 0) return QG_OK;
+  if (!x_f16 || !prepared || !aligned16(x_f16) || !aligned16(prepared)) return QG_ERR_INVALID_ARG;
+  if (prepared_bytes < w4a8_layout(M, K).total) return QG_ERR_WORKSPACE;
+  clear_stale_error();
+  return prepare_impl(x_f16, M, K, ldx, prepared, nullptr, as_stream(stream));
+}
+
+int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, const void* w_packed,
+                       const void* s_packed, void* y_f16, void* stream) {
+  int st = check_w4a8_shape(M, K, N);
+  if (st != QG_OK) return st;
+  if ((st = check_ptrs(M, prepared, w_packed, s_packed, y_f16)) != QG_OK) return st;
+  if (M == 0) return QG_OK;
+  clear_stale_error();
+  return gemm_prepared_impl(prepared, M, K, N, w_packed, s_packed, y_f16, as_stream(stream), nullptr, 0, 0, 0, 0);
 }
 
 int w8a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const int8_t* w,

@@ -20,8 +20,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // the C-ABI layer before any of these is called.
 // ---------------------------------------------------------------------------
 
+// Per-token int8 quantisation.  Codes go to q (row-major, leading dimension
+// ldq) when q is not null and to qfrag in the fragment order the
+// weight-streaming W4A8 kernel reads when qfrag is not null.
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                            int8_t* q, int64_t ldq, float* scale, hipStream_t st);
+                            int8_t* q, int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st);
 
 hipError_t launch_w4_repack(const int8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                             void* w_packed, uint16_t* s_packed, hipStream_t st);
@@ -29,20 +32,22 @@ hipError_t launch_w4_repack(const int8_t* codes, const uint16_t* scales, int64_t
 // Operating modes of the skinny (M <= 64) GEMM kernel.
 enum SkinnyMode { kW4A8 = 0, kW4A16 = 1, kW8A16 = 2 };
 
-// Split-K factor the skinny kernel uses for an [*, K] x [N, K] product; a
-// pure function of (N, K) so workspace sizing and launch agree.
-int skinny_splits(int64_t N, int64_t K);
+// Work decomposition of the skinny kernel: n-tiles (16 columns) per
+// workgroup.  A pure function of the operation and shape.
+struct SkinnyPlan {
+  int nt;       // n-tiles per workgroup: 1, 2 or 4
+};
+SkinnyPlan skinny_plan(int mode, int64_t N, int64_t K);
 
 struct SkinnyArgs {
   int mode;
-  const void* act;          // W4A8: int8 codes [M][lda]; W4A16 / W8A16: fp16 [M][lda]
+  const void* act;          // W4A8: int8 codes in fragment order; W4A16 / W8A16: fp16 [M][lda]
   int64_t lda;
   const float* tok_scale;   // W4A8 token scales [M]
   const void* w;            // packed int4 (W4A8/W4A16) or row-major int8 [N][K] (W8A16)
   const uint16_t* s;        // packed scales (W4A*) or row-major fp16 [N][K/128] (W8A16)
   int64_t M, N, K;
   uint16_t* y;              // fp16 [M][N]
-  float* partials;          // [splits][M][N] fp32 when splits > 1
   int32_t* dbg;             // W4A8 debug window (may be null)
   int64_t dm0, dm1, dn0, dn1;
 };

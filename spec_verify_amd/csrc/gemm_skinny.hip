@@ -7,15 +7,14 @@
 // README, "What each step buys" (W4A16 body).  At these M the product reads
 // each weight byte once and does little arithmetic per byte, so the kernel is
 // built to keep HBM busy: every wavefront streams 1 KiB weight blocks with
-// 128-bit loads, one group ahead of the matrix-core work.
+// 128-bit buffer loads, several groups ahead of the matrix-core work.
 //
-// Work split.  A workgroup (4 wavefronts) owns 64 output columns (4 n-tiles
-// of 16 rows of W) and a contiguous range of K groups ("split"); its waves
-// take that range's groups round-robin, so every activation byte is read once
-// per workgroup.  The four waves' fp32 sums are added in LDS in a fixed
-// order; with more than one split, each split writes fp32 partial sums and a
-// second kernel adds the splits in index order.  No floating-point atomics:
-// results are bit-reproducible.
+// Work split.  A workgroup of NW wavefronts owns NT n-tiles (16 output
+// columns = 16 rows of W each) over all of K; its waves take the K groups
+// round-robin, so every weight and activation byte is read once per
+// workgroup, and their fp32 sums meet in LDS in a fixed tree order (results
+// are bit-reproducible; no atomics).  More waves per workgroup means fewer
+// groups, and so fewer dependent memory round trips, per wave.
 //
 // Matrix-core mapping.  Weights are the A operand (rows n), activations the B
 // operand (columns m), so a 16x16 output tile lands as 4 consecutive n for
@@ -26,22 +25,22 @@
 //          then acc += group_sum * s_w
 //   W8A16  as W4A16 with int8 table codes converted exactly to fp16.
 // The k order inside a lane operand is a permutation shared by both operands,
-// so the contraction is unaffected by it.
+// so the contraction is unaffected by it.  W4A8 reads its activation codes
+// in fragment order (see act_quant.hip): each 16-byte lane operand of a
+// 16-row m-tile is contiguous, so one load instruction moves 1 KiB.
 #include "common.h"
 
 namespace qg {
 namespace {
 
 struct SkinnyParams {
-  const void* act;
+  const void* act;          // W4A8: codes in fragment order; else fp16 [M][lda]
   int64_t lda;
   const float* tok_scale;
   const void* w;
   const uint16_t* s;
   int M, N, K, G;
-  int splits, gps;          // number of K splits, groups per split
   uint16_t* y;
-  float* partials;
   int32_t* dbg;
   int dm0, dm1, dn0, dn1;
 };
@@ -59,17 +58,24 @@ __device__ __forceinline__ i32x4 w4_to_i8x16(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// Exact fp16 values of the 8 int4 codes of one packed word:
-// 0x6400 | (nibble ^ 8) is the fp16 number 1024 + q + 8.  Element order is
-// k offsets {0, 2, 4, 6, 1, 3, 5, 7} (see kW4A16 activation shuffle).
+// Exact fp16 values of the 8 int4 codes of one packed word.  With
+// u = nibble ^ 8 = q + 8, the pattern 0x6400 | u is the fp16 number 1024 + u
+// and 0x6400 | (u << 4) is 1024 + 16 u; so (v - 1032) and (v / 16 - 72) are
+// q exactly.  One shift by 8 serves slots 2, 3, 6, 7.  Element order is
+// slots {0, 4, 1, 5, 2, 6, 3, 7} = k offsets {0, 2, 4, 6, 1, 3, 5, 7} (the
+// activation operand is shuffled to match).
 __device__ __forceinline__ f16x8 w4_to_f16x8(uint32_t w) {
   const uint32_t x = w ^ 0x88888888u;
+  const uint32_t y = x >> 8;
   u32x4 p;
   p[0] = (x & 0x000F000Fu) | 0x64006400u;
-  p[1] = ((x >> 4) & 0x000F000Fu) | 0x64006400u;
-  p[2] = ((x >> 8) & 0x000F000Fu) | 0x64006400u;
-  p[3] = ((x >> 12) & 0x000F000Fu) | 0x64006400u;
-  return __builtin_bit_cast(f16x8, p) - (f16x8)(_Float16)1032.0f;
+  p[1] = (x & 0x00F000F0u) | 0x64006400u;
+  p[2] = (y & 0x000F000Fu) | 0x64006400u;
+  p[3] = (y & 0x00F000F0u) | 0x64006400u;
+  const f16x8 v = __builtin_bit_cast(f16x8, p);
+  const f16x8 mul = {1.0f16, 1.0f16, 0.0625f16, 0.0625f16, 1.0f16, 1.0f16, 0.0625f16, 0.0625f16};
+  const f16x8 add = {-1032.0f16, -1032.0f16, -72.0f16, -72.0f16, -1032.0f16, -1032.0f16, -72.0f16, -72.0f16};
+  return v * mul + add;
 }
 
 // Exact fp16 values of 8 int8 codes (natural order): byte b ^ 0x80 = b + 128
@@ -84,109 +90,100 @@ __device__ __forceinline__ f16x8 i8_to_f16x8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(f16x8, p) - (f16x8)(_Float16)1152.0f;
 }
 
-template <int MODE, int MT>
+// One pipeline stage: one 128-wide group's weights and scales for the NT
+// n-tiles of the workgroup and the matching activation fragments.
+template <int MODE, int NT, int MT>
 struct Stage;
 
-template <int MT>
-struct Stage<kW4A8, MT> {
-  uint4 w[4];
-  uint2 s[4];
+template <int NT, int MT>
+struct Stage<kW4A8, NT, MT> {
+  uint4 w[NT];
   i32x4 x[MT][2];
 };
 
-template <int MT>
-struct Stage<kW4A16, MT> {
-  uint4 w[4];
-  uint2 s[4];
+template <int NT, int MT>
+struct Stage<kW4A16, NT, MT> {
+  uint4 w[NT];
   f16x8 x[MT][4];
 };
 
-template <int MT>
-struct Stage<kW8A16, MT> {
-  uint4 w[4][2];
-  uint16_t s[4][4];
+template <int NT, int MT>
+struct Stage<kW8A16, NT, MT> {
+  uint4 w[NT][2];
   f16x8 x[MT][4];
 };
 
-template <int MODE, int MT>
-__device__ __forceinline__ void load_stage(const SkinnyParams& p, Stage<MODE, MT>& st, int g, int nt0,
-                                           int nvalid, int lane) {
+// Buffer resources over the bytes one workgroup may read.  Loads use the
+// hardware range check: a row past M, an n-tile past N or a pipeline stage
+// past the wave's last group is an out-of-range offset, which returns zeros
+// without touching memory.  That keeps every load unconditional, so the
+// prefetch ring is branch-free and the compiler counts outstanding loads
+// exactly.
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t w, x;
+};
+
+constexpr uint32_t kOOB = 0x80000000u;   // beyond every resource's extent (checked on the host)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int MODE, int NT, int MT>
+__device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs, Stage<MODE, NT, MT>& st,
+                                           bool valid, int g, int lane) {
   const int col = lane & 15, quad = lane >> 4;
-  const int G = p.G;
+  const uint32_t G = (uint32_t)p.G;
+  const uint32_t bad = valid ? 0u : kOOB;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j < nvalid) {
-      const int64_t blk = (int64_t)(nt0 + j) * G + g;
-      if constexpr (MODE == kW8A16) {
-        const int8_t* row = reinterpret_cast<const int8_t*>(p.w) +
-                            ((int64_t)(nt0 + j) * 16 + col) * p.K + g * kGroup + 16 * quad;
-        st.w[j][0] = *reinterpret_cast<const uint4*>(row);
-        st.w[j][1] = *reinterpret_cast<const uint4*>(row + 64);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          st.s[j][r] = p.s[((int64_t)(nt0 + j) * 16 + 4 * quad + r) * G + g];
-      } else {
-        st.w[j] = reinterpret_cast<const uint4*>(p.w)[blk * 64 + lane];
-        st.s[j] = *reinterpret_cast<const uint2*>(p.s + blk * 16 + 4 * quad);
-      }
+  for (int j = 0; j < NT; ++j) {
+    if constexpr (MODE == kW8A16) {
+      const uint32_t row = (uint32_t)(j * 16 + col) * (uint32_t)p.K + (uint32_t)g * kGroup + 16u * quad;
+      st.w[j][0] = ld128(rs.w, row + bad);
+      st.w[j][1] = ld128(rs.w, row + 64u + bad);
     } else {
-      if constexpr (MODE == kW8A16) {
-        st.w[j][0] = st.w[j][1] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st.s[j][r] = 0;
-      } else {
-        st.w[j] = make_uint4(0, 0, 0, 0);
-        st.s[j] = make_uint2(0, 0);
-      }
+      const uint32_t blk = (uint32_t)j * G + (uint32_t)g;
+      st.w[j] = ld128(rs.w, (blk * 64u + lane) * 16u + bad);
     }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + col;
+    const uint32_t m = (uint32_t)(mt * 16 + col);
     if constexpr (MODE == kW4A8) {
-      if (m < p.M) {
-        const int8_t* src = reinterpret_cast<const int8_t*>(p.act) + (int64_t)m * p.lda + g * kGroup + 16 * quad;
-        st.x[mt][0] = *reinterpret_cast<const i32x4*>(src);
-        st.x[mt][1] = *reinterpret_cast<const i32x4*>(src + 64);
-      } else {
-        st.x[mt][0] = st.x[mt][1] = (i32x4)0;
-      }
+      const uint32_t off = ((((uint32_t)mt * G + (uint32_t)g) * 2u) * 64u + lane) * 16u + bad;
+      st.x[mt][0] = __builtin_bit_cast(i32x4, ld128(rs.x, off));
+      st.x[mt][1] = __builtin_bit_cast(i32x4, ld128(rs.x, off + 1024u));
     } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (m < p.M) {
-          const uint16_t* src = reinterpret_cast<const uint16_t*>(p.act) + (int64_t)m * p.lda + g * kGroup +
-                                64 * (t >> 1) + 16 * quad + 8 * (t & 1);
-          const f16x8 v = *reinterpret_cast<const f16x8*>(src);
-          if constexpr (MODE == kW4A16)
-            st.x[mt][t] = __builtin_shufflevector(v, v, 0, 2, 4, 6, 1, 3, 5, 7);
-          else
-            st.x[mt][t] = v;
-        } else {
-          st.x[mt][t] = (f16x8)(_Float16)0.0f;
-        }
+        const uint32_t off =
+            (m * (uint32_t)p.lda + (uint32_t)g * kGroup + 64u * (t >> 1) + 16u * quad + 8u * (t & 1)) * 2u + bad;
+        st.x[mt][t] = __builtin_bit_cast(f16x8, ld128(rs.x, off));
       }
     }
   }
 }
 
-template <int MODE, int MT, bool DEBUG>
-__device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage<MODE, MT>& st, int g,
-                                              int nt0, int nvalid, int lane, f32x4 (&acc)[4][MT]) {
+// Group scales live in LDS as [group][column of the workgroup] fp16; a
+// stage past the wave's last group reads group 0's (its products are zero).
+template <int MODE, int NT, int MT, bool DEBUG>
+__device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage<MODE, NT, MT>& st, int g,
+                                              bool gvalid, int nt0, int lane, const uint16_t* lds_s,
+                                              f32x4 (&acc)[NT][MT]) {
   const int col = lane & 15, quad = lane >> 4;
+  const int gs = gvalid ? g : 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j >= nvalid) continue;
+  for (int j = 0; j < NT; ++j) {
+    const uint2 sv = *reinterpret_cast<const uint2*>(lds_s + gs * (16 * NT) + j * 16 + 4 * quad);
     float sc[4];
-    if constexpr (MODE == kW8A16) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = half_bits_to_float(st.s[j][r]);
-    } else {
-      sc[0] = half_bits_to_float(st.s[j].x & 0xFFFFu);
-      sc[1] = half_bits_to_float(st.s[j].x >> 16);
-      sc[2] = half_bits_to_float(st.s[j].y & 0xFFFFu);
-      sc[3] = half_bits_to_float(st.s[j].y >> 16);
-    }
+    sc[0] = half_bits_to_float(sv.x & 0xFFFFu);
+    sc[1] = half_bits_to_float(sv.x >> 16);
+    sc[2] = half_bits_to_float(sv.y & 0xFFFFu);
+    sc[3] = half_bits_to_float(sv.y >> 16);
     if constexpr (MODE == kW4A8) {
       const i32x4 a0 = w4_to_i8x16(st.w[j].x, st.w[j].y);
       const i32x4 a1 = w4_to_i8x16(st.w[j].z, st.w[j].w);
@@ -200,11 +197,11 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
         for (int r = 0; r < 4; ++r) acc[j][mt][r] = fmaf((float)P[r], sc[r], acc[j][mt][r]);
         if constexpr (DEBUG) {
           const int m = mt * 16 + col;
-          if (m >= p.dm0 && m < p.dm1 && m < p.M) {
+          if (gvalid && m >= p.dm0 && m < p.dm1 && m < p.M) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int n = (nt0 + j) * 16 + 4 * quad + r;
-              if (n >= p.dn0 && n < p.dn1)
+              if (n >= p.dn0 && n < p.dn1 && n < p.N)
                 p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * p.G + g] = P[r] >> 4;
             }
           }
@@ -225,10 +222,19 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f32x4 gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], st.x[mt][0], (f32x4)0.0f, 0, 0, 0);
-        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], st.x[mt][1], gs, 0, 0, 0);
-        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], st.x[mt][2], gs, 0, 0, 0);
-        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], st.x[mt][3], gs, 0, 0, 0);
+        f16x8 b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // W4A16 weight elements come in k order {0,2,4,6,1,3,5,7}; match it.
+          if constexpr (MODE == kW4A16)
+            b[t] = __builtin_shufflevector(st.x[mt][t], st.x[mt][t], 0, 2, 4, 6, 1, 3, 5, 7);
+          else
+            b[t] = st.x[mt][t];
+        }
+        f32x4 gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[0], (f32x4)0.0f, 0, 0, 0);
+        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b[1], gs, 0, 0, 0);
+        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], b[2], gs, 0, 0, 0);
+        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], b[3], gs, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][mt][r] = fmaf(gs[r], sc[r], acc[j][mt][r]);
       }
@@ -236,113 +242,212 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
   }
 }
 
-template <int MODE, int MT, bool DEBUG>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyParams p) {
+template <int MODE, int NT, int MT, int NW, int PF, bool DEBUG>
+__global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int split = blockIdx.x % p.splits;
-  const int nb = blockIdx.x / p.splits;
-  const int g0 = split * p.gps;
-  const int g1 = min(p.G, g0 + p.gps);
-  const int nt0 = nb * 4;
-  const int nvalid = min(4, p.N / 16 - nt0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
+  const int nt0 = blockIdx.x * NT;
+  const int nvalid = min(NT, p.N / 16 - nt0);
 
-  f32x4 acc[4][MT];
+  f32x4 acc[NT][MT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4)0.0f;
 
-  int g = g0 + wave;
-  if (g < g1) {
-    Stage<MODE, MT> cur;
-    load_stage<MODE, MT>(p, cur, g, nt0, nvalid, lane);
-    for (; g < g1; g += 4) {
-      Stage<MODE, MT> nxt;
-      const bool more = g + 4 < g1;
-      if (more) load_stage<MODE, MT>(p, nxt, g + 4, nt0, nvalid, lane);
-      compute_stage<MODE, MT, DEBUG>(p, cur, g, nt0, nvalid, lane, acc);
-      if (more) cur = nxt;
+  Rsrc rs;
+  {
+    const int64_t G = p.G;
+    if constexpr (MODE == kW8A16)
+      rs.w = make_rsrc(reinterpret_cast<const int8_t*>(p.w) + (int64_t)nt0 * 16 * p.K,
+                       (uint32_t)(nvalid * 16 * (int64_t)p.K));
+    else
+      rs.w = make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (int64_t)nt0 * G * 1024, (uint32_t)(nvalid * G * 1024));
+    if constexpr (MODE == kW4A8)
+      rs.x = make_rsrc(p.act, (uint32_t)((int64_t)((p.M + 15) / 16) * 16 * p.K));
+    else
+      rs.x = make_rsrc(p.act, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+  }
+
+  // The workgroup's group scales (NT*16 columns x G groups, one contiguous
+  // block in both scale layouts) go to LDS once, transposed to
+  // [group][column]; the loads are issued before the weight prefetch so the
+  // barrier below waits for them only.
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_s[];
+  constexpr int COLS = 16 * NT;
+  const int nsc = nvalid * 16 * p.G;           // scales of the valid columns
+  const uint16_t* sbase = MODE == kW8A16 ? p.s + (int64_t)nt0 * 16 * p.G : p.s + (int64_t)nt0 * p.G * 16;
+  constexpr int SPT = 8;                       // scales per thread per pass (one 16-byte load)
+  uint4 sreg[4];
+  const int npass = (nsc + 64 * NW * SPT - 1) / (64 * NW * SPT);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sbase, (uint32_t)nsc * 2u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sreg[i] = ld128(srs, (uint32_t)(threadIdx.x + 64 * NW * i) * SPT * 2u);
+  for (int i = 4; i < npass; ++i) {            // very long K: load and store directly
+    const int e = (threadIdx.x + 64 * NW * i) * SPT;
+    if (e < nsc) {
+      const uint4 v = *reinterpret_cast<const uint4*>(sbase + e);
+      const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                             (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int idx = e + t;
+        int c, g;
+        if constexpr (MODE == kW8A16) { c = idx / p.G; g = idx % p.G; }
+        else { c = (idx / (16 * p.G)) * 16 + idx % 16; g = (idx / 16) % p.G; }
+        lds_s[g * COLS + c] = h[t];
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // This wave's groups are wave, wave + NW, ...; PF of them are in flight in
+  // a register ring.  Scheduling barriers keep each stage's multiply after
+  // the previous stage's loads, so a stage waits only for its own data.  The
+  // last round issues no loads, so nothing is fetched past the last group.
+  const int ng = wave < p.G ? (p.G - wave + NW - 1) / NW : 0;
+  const int rounds = (ng + PF - 1) / PF;
+  // Each workgroup walks its wave's groups from a different starting point,
+  // so concurrent workgroups do not all read the same activation columns
+  // (the same L2 lines) at the same moment.
+  const int rot = ng > 0 ? (int)(blockIdx.x % (unsigned)ng) : 0;
+  auto gidx = [&](int i) { return wave + NW * (i < ng ? (i + rot < ng ? i + rot : i + rot - ng) : i); };
+  Stage<MODE, NT, MT> st[PF];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    load_stage<MODE, NT, MT>(p, rs, st[s], s < ng, gidx(s), lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (threadIdx.x + 64 * NW * i) * SPT;
+    if (i < npass && e < nsc) {
+      const uint16_t h[8] = {(uint16_t)sreg[i].x, (uint16_t)(sreg[i].x >> 16), (uint16_t)sreg[i].y,
+                             (uint16_t)(sreg[i].y >> 16), (uint16_t)sreg[i].z, (uint16_t)(sreg[i].z >> 16),
+                             (uint16_t)sreg[i].w, (uint16_t)(sreg[i].w >> 16)};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int idx = e + t;
+        int c, g;
+        if constexpr (MODE == kW8A16) { c = idx / p.G; g = idx % p.G; }
+        else { c = (idx / (16 * p.G)) * 16 + idx % 16; g = (idx / 16) % p.G; }
+        lds_s[g * COLS + c] = h[t];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int r = 0; r + 1 < rounds; ++r) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int ii = r * PF + s;
+      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), true, nt0, lane, lds_s, acc);
+      // Stages past the last group load nothing (out-of-range offsets) and
+      // multiply zeros, which keeps this loop free of branches.
+      load_stage<MODE, NT, MT>(p, rs, st[s], ii + PF < ng, gidx(ii + PF), lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (rounds > 0) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int ii = (rounds - 1) * PF + s;
+      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), ii < ng, nt0, lane, lds_s, acc);
     }
   }
 
-  // Fixed-order sum of the four waves' partial results.
-  __shared__ float red[4][4 * MT * 4][64];
+  // Fixed-order tree sum over the waves: at each level the upper half of the
+  // remaining waves hands its sums to the lower half through LDS.
+  constexpr int E = NT * MT * 4;
+  if constexpr (NW > 1) {
+    __shared__ float red[NW / 2][E][64];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+      if (wave >= half && wave < 2 * half) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][(j * MT + mt) * 4 + r][lane] = acc[j][mt][r];
-  __syncthreads();
-
-  for (int idx = threadIdx.x; idx < 4 * MT * 64; idx += 256) {
-    const int l = idx & 63, jm = idx >> 6;
-    const int j = jm / MT, mt = jm % MT;
-    const int m = mt * 16 + (l & 15);
-    if (j >= nvalid || m >= p.M) continue;
-    const int n = (nt0 + j) * 16 + 4 * (l >> 4);
-    float v[4];
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = jm * 4 + r;
-      v[r] = ((red[0][e][l] + red[1][e][l]) + red[2][e][l]) + red[3][e][l];
+            for (int r = 0; r < 4; ++r) red[wave - half][(j * MT + mt) * 4 + r][lane] = acc[j][mt][r];
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][mt][r] += red[wave][(j * MT + mt) * 4 + r][lane];
+      }
+      if (half > 1) __syncthreads();
     }
-    if (p.splits == 1) {
-      const float ts = MODE == kW4A8 ? p.tok_scale[m] : 1.0f;
+  }
+  if (wave != 0) return;
+
+  const int col = lane & 15, quad = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + col;
+    if (m >= p.M) continue;
+    const float ts = MODE == kW4A8 ? p.tok_scale[m] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (j >= nvalid) continue;
+      const int n = (nt0 + j) * 16 + 4 * quad;
       uint2 o;
-      o.x = (uint32_t)float_to_half_bits(v[0] * ts) | ((uint32_t)float_to_half_bits(v[1] * ts) << 16);
-      o.y = (uint32_t)float_to_half_bits(v[2] * ts) | ((uint32_t)float_to_half_bits(v[3] * ts) << 16);
+      o.x = (uint32_t)float_to_half_bits(acc[j][mt][0] * ts) | ((uint32_t)float_to_half_bits(acc[j][mt][1] * ts) << 16);
+      o.y = (uint32_t)float_to_half_bits(acc[j][mt][2] * ts) | ((uint32_t)float_to_half_bits(acc[j][mt][3] * ts) << 16);
       *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.N + n) = o;
-    } else {
-      *reinterpret_cast<float4*>(p.partials + ((int64_t)split * p.M + m) * p.N + n) =
-          make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
 
-// y[m][n] = fp16(tok[m] * sum_{s < S} part[s][m][n]), splits added in index order.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M,
-                                                            int N, const float* __restrict__ tok,
-                                                            uint16_t* __restrict__ y) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)M * (N / 4);
-  if (idx >= total) return;
-  const int m = (int)(idx / (N / 4));
-  const int64_t off = (int64_t)m * N + 4 * (idx % (N / 4));
-  float4 a = *reinterpret_cast<const float4*>(part + off);
-  for (int s = 1; s < S; ++s) {
-    const float4 b = *reinterpret_cast<const float4*>(part + (int64_t)s * M * N + off);
-    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+// Prefetch depth: deep enough to keep several 1 KiB weight blocks per wave
+// in flight, shallow enough to leave room for two waves per SIMD.
+template <int MODE, int NT, int MT>
+constexpr int prefetch_depth() {
+  return MODE == kW4A8 ? (NT * MT <= 4 ? 5 : 3) : 2;
+}
+
+template <int MODE, int NT, int NW, bool DEBUG>
+void launch_mt(const SkinnyParams& p, int mt, dim3 grid, hipStream_t st) {
+  const dim3 block(64 * NW);
+  const size_t lds = (size_t)16 * NT * p.G * 2;   // the workgroup's group scales
+  switch (mt) {
+    case 1: skinny_kernel<MODE, NT, 1, NW, prefetch_depth<MODE, NT, 1>(), DEBUG><<<grid, block, lds, st>>>(p); break;
+    case 2: skinny_kernel<MODE, NT, 2, NW, prefetch_depth<MODE, NT, 2>(), DEBUG><<<grid, block, lds, st>>>(p); break;
+    case 3: skinny_kernel<MODE, NT, 3, NW, prefetch_depth<MODE, NT, 3>(), DEBUG><<<grid, block, lds, st>>>(p); break;
+    default: skinny_kernel<MODE, NT, 4, NW, prefetch_depth<MODE, NT, 4>(), DEBUG><<<grid, block, lds, st>>>(p); break;
   }
-  const float ts = tok ? tok[m] : 1.0f;
-  uint2 o;
-  o.x = (uint32_t)float_to_half_bits(a.x * ts) | ((uint32_t)float_to_half_bits(a.y * ts) << 16);
-  o.y = (uint32_t)float_to_half_bits(a.z * ts) | ((uint32_t)float_to_half_bits(a.w * ts) << 16);
-  *reinterpret_cast<uint2*>(y + off) = o;
 }
 
 template <int MODE, bool DEBUG>
-hipError_t launch_mode(const SkinnyParams& p, int mt, dim3 grid, hipStream_t st) {
-  switch (mt) {
-    case 1: skinny_kernel<MODE, 1, DEBUG><<<grid, 256, 0, st>>>(p); break;
-    case 2: skinny_kernel<MODE, 2, DEBUG><<<grid, 256, 0, st>>>(p); break;
-    case 3: skinny_kernel<MODE, 3, DEBUG><<<grid, 256, 0, st>>>(p); break;
-    default: skinny_kernel<MODE, 4, DEBUG><<<grid, 256, 0, st>>>(p); break;
-  }
+hipError_t launch_mode(const SkinnyParams& p, const SkinnyPlan& pl, int mt, dim3 grid, hipStream_t st) {
+  if (pl.nt == 1)
+    launch_mt<MODE, 1, 8, DEBUG>(p, mt, grid, st);
+  else if (pl.nt == 2)
+    launch_mt<MODE, 2, 8, DEBUG>(p, mt, grid, st);
+  else
+    launch_mt<MODE, 4, 4, DEBUG>(p, mt, grid, st);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int skinny_splits(int64_t N, int64_t K) {
-  const int64_t nblocks = (N / 16 + 3) / 4;
-  const int64_t G = K / kGroup;
-  int s = 1;
-  // Split K until the grid covers the 256 compute units, keeping at least
-  // two groups per wavefront in every split.
-  while (nblocks * s < 256 && G / (2 * s) >= 8) s *= 2;
-  return s;
+SkinnyPlan skinny_plan(int mode, int64_t N, int64_t K) {
+  (void)K;
+  const int64_t ntiles = N / 16;
+  SkinnyPlan pl;
+  // Few output tiles (decode-sized N): one or two n-tiles per workgroup with
+  // eight waves splitting K, so enough workgroups exist and each wave has a
+  // short chain of groups.  Many tiles (wide projections, the lm_head): four
+  // n-tiles per workgroup, four waves.
+  if (mode == kW4A8 && ntiles <= 1024)
+    pl.nt = 2;
+  else
+    pl.nt = 4;
+  return pl;
 }
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
@@ -357,28 +462,18 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.N = (int)a.N;
   p.K = (int)a.K;
   p.G = (int)(a.K / kGroup);
-  p.splits = skinny_splits(a.N, a.K);
-  p.gps = (p.G + p.splits - 1) / p.splits;
   p.y = a.y;
-  p.partials = a.partials;
   p.dbg = a.dbg;
   p.dm0 = (int)a.dm0; p.dm1 = (int)a.dm1; p.dn0 = (int)a.dn0; p.dn1 = (int)a.dn1;
-  const int nblocks = (p.N / 16 + 3) / 4;
-  const dim3 grid((unsigned)(nblocks * p.splits));
+  const SkinnyPlan pl = skinny_plan(a.mode, a.N, a.K);
+  const dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
   const int mt = (p.M + 15) / 16;
-  hipError_t e;
   switch (a.mode) {
     case kW4A8:
-      e = a.dbg ? launch_mode<kW4A8, true>(p, mt, grid, st) : launch_mode<kW4A8, false>(p, mt, grid, st);
-      break;
-    case kW4A16: e = launch_mode<kW4A16, false>(p, mt, grid, st); break;
-    default: e = launch_mode<kW8A16, false>(p, mt, grid, st); break;
+      return a.dbg ? launch_mode<kW4A8, true>(p, pl, mt, grid, st) : launch_mode<kW4A8, false>(p, pl, mt, grid, st);
+    case kW4A16: return launch_mode<kW4A16, false>(p, pl, mt, grid, st);
+    default: return launch_mode<kW8A16, false>(p, pl, mt, grid, st);
   }
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t total = (int64_t)p.M * (p.N / 4);
-  splitk_reduce_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
-      p.partials, p.splits, p.M, p.N, a.mode == kW4A8 ? p.tok_scale : nullptr, p.y);
-  return hipGetLastError();
 }
 
 }  // namespace qg

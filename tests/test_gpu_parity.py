@@ -291,6 +291,35 @@ def test_repeat_runs_are_bit_identical(qg, name):
     assert np.array_equal(bits(a), bits(b))
 
 
+@pytest.mark.parametrize("M,K,N", [(64, 5120, 5120), (3, 256, 48), (130, 384, 144)])
+def test_prepared_activations_are_reusable_and_match_the_one_call_path(qg, M, K, N):
+    """One w4a8_prepare feeding two GEMMs (different weights) gives exactly
+    w4a8_gemm's outputs for each."""
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=21)
+    xd = dev(x)
+    prep = qg.w4a8_prepare(xd)
+    for seed in (22, 23):
+        codes, scales = synth.weights(N, K, seed=seed)
+        wp, sp = packed(qg, codes, scales)
+        a = host(qg.w4a8_gemm_prepared(prep, M, K, wp, sp, N))
+        b = host(qg.w4a8_gemm(xd, wp, sp, N))
+        assert np.array_equal(bits(a), bits(b))
+        assert_bounds(a, oracle.ref_w4a8(x, codes, scales))
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 5120, 5120), (5, 5120, 144), (100, 512, 272)])
+def test_w4a8_workspace_reuse_across_weight_sets(qg, M, K, N):
+    """One workspace reused for different inputs and weights gives each
+    call's own result (nothing stale carries over between calls)."""
+    ws = torch.empty((qg.qg_workspace_bytes(qg.QG_OP_W4A8, M, K, N),), dtype=torch.uint8, device=DEV)
+    for seed in (11, 12, 11):
+        x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=seed)
+        codes, scales = synth.weights(N, K, seed=seed + 1)
+        wp, sp = packed(qg, codes, scales)
+        y = qg.w4a8_gemm(dev(x), wp, sp, N, workspace=ws)
+        assert_bounds(host(y), oracle.ref_w4a8(x, codes, scales), f"seed {seed}")
+
+
 @pytest.mark.parametrize("M,N", [(3, 48), (64, 80), (130, 144)])
 def test_outputs_stay_inside_their_buffer(qg, M, N):
     """Canary-filled padding around y is untouched after the call."""
