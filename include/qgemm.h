@@ -45,7 +45,7 @@ extern "C" {
 /* Status codes returned by every int-returning entry point. */
 #define QG_OK 0
 #define QG_ERR_INVALID_ARG 1       /* null/misaligned pointer, negative size, ldx < K, bad op */
-#define QG_ERR_UNSUPPORTED_SHAPE 2 /* K % 128 != 0, N % 16 != 0, H % 128 != 0, size too large */
+#define QG_ERR_UNSUPPORTED_SHAPE 2 /* K % 128 != 0, N % 16 != 0, H % 128 != 0, K > 2^22, size too large */
 #define QG_ERR_WORKSPACE 3         /* ws_bytes smaller than qg_workspace_bytes() */
 #define QG_ERR_LAUNCH 4            /* the HIP runtime reported an error at launch */
 

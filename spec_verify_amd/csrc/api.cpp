@@ -12,6 +12,9 @@ namespace {
 using qg::kGroup;
 
 constexpr int64_t kMaxDim = INT32_MAX;     // kernels index rows/columns with 32-bit ints
+// Longest K: the kernels address one workgroup's operand block (up to 128
+// rows of K bytes, or 64 rows of K fp16) with 32-bit buffer offsets.
+constexpr int64_t kMaxK = int64_t(1) << 22;
 constexpr int64_t kSkinnyMaxM = 64;         // largest M the weight-streaming kernel takes per launch
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -36,8 +39,8 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
 int check_gemm_shape(int64_t M, int64_t K, int64_t N, int64_t ldx) {
   if (M < 0 || K <= 0 || N <= 0) return QG_ERR_INVALID_ARG;
   if (K % kGroup != 0 || N % 16 != 0) return QG_ERR_UNSUPPORTED_SHAPE;
-  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
-  if (ldx < K || ldx % 8 != 0) return QG_ERR_INVALID_ARG;
+  if (M > kMaxDim || K > kMaxK || N > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < K || ldx % 8 != 0 || ldx > kMaxK) return QG_ERR_INVALID_ARG;
   return QG_OK;
 }
 
@@ -96,7 +99,7 @@ int gemm_streaming(int mode, const void* x, int64_t M, int64_t K, int64_t N, int
 int check_w4a8_shape(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K <= 0 || N <= 0) return QG_ERR_INVALID_ARG;
   if (K % kGroup != 0 || N % 16 != 0) return QG_ERR_UNSUPPORTED_SHAPE;
-  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (M > kMaxDim || K > kMaxK || N > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;
   return QG_OK;
 }
 
