@@ -45,7 +45,7 @@ extern "C" {
 /* Status codes returned by every int-returning entry point. */
 #define QG_OK 0
 #define QG_ERR_INVALID_ARG 1       /* null/misaligned pointer, negative size, ldx < K, bad op */
-#define QG_ERR_UNSUPPORTED_SHAPE 2 /* K % 128 != 0, N % 16 != 0, H % 128 != 0, K > 2^22, size too large */
+#define QG_ERR_UNSUPPORTED_SHAPE 2 /* K % 128 != 0, N % 16 != 0, H % 128 != 0, K too long, size too large */
 #define QG_ERR_WORKSPACE 3         /* ws_bytes smaller than qg_workspace_bytes() */
 #define QG_ERR_LAUNCH 4            /* the HIP runtime reported an error at launch */
 
@@ -110,6 +110,8 @@ int w4_repack(const int8_t* codes, const void* scales_f16, int64_t N, int64_t K,
  *             products of fp16 x and exact int4 codes accumulated in fp32,
  *             each 128-wide group rescaled by its fp32 scale.
  *   workspace, ws_bytes  unused (qg_workspace_bytes gives 0); may be NULL, 0
+ *   K <= 65536 (for w8a16_gemm too): the kernel holds a workgroup's group
+ *   scales in LDS; a longer K returns QG_ERR_UNSUPPORTED_SHAPE.
  */
 int w4a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
                const void* w_packed, const void* s_packed, void* y_f16,

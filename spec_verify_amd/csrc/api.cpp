@@ -16,6 +16,9 @@ constexpr int64_t kMaxDim = INT32_MAX;     // kernels index rows/columns with 32
 // rows of K bytes, or 64 rows of K fp16) with 32-bit buffer offsets.
 constexpr int64_t kMaxK = int64_t(1) << 22;
 constexpr int64_t kSkinnyMaxM = 64;         // largest M the weight-streaming kernel takes per launch
+// Longest K of w4a16_gemm / w8a16_gemm: their kernel keeps a workgroup's
+// group scales (64 columns x K/128 groups of fp16) in LDS.
+constexpr int64_t kMaxK16 = 65536;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -72,6 +75,7 @@ int gemm_streaming(int mode, const void* x, int64_t M, int64_t K, int64_t N, int
                    const void* w, const void* s, void* y, void* ws, size_t ws_bytes, void* stream) {
   int st = check_gemm_shape(M, K, N, ldx);
   if (st != QG_OK) return st;
+  if (K > kMaxK16) return QG_ERR_UNSUPPORTED_SHAPE;
   if ((st = check_ptrs(M, x, w, s, y)) != QG_OK) return st;
   if (M == 0) return QG_OK;
   (void)ws;
@@ -219,7 +223,7 @@ size_t qg_workspace_bytes(int op, int64_t M, int64_t K, int64_t N) {
   switch (op) {
     case QG_OP_W4A8: return M == 0 ? 0 : w4a8_layout(M, K).total;
     case QG_OP_W4A16:
-    case QG_OP_W8A16: return 0;
+    case QG_OP_W8A16: return K > kMaxK16 ? (size_t)-1 : 0;
     default: return (size_t)-1;
   }
 }

@@ -12,15 +12,17 @@
 // Work split.  A workgroup of NW wavefronts owns NT n-tiles (16 output
 // columns = 16 rows of W each) over all of K; its waves take the K groups
 // round-robin, so every weight and activation byte is read once per
-// workgroup, and their fp32 sums meet in LDS in a fixed tree order (results
-// are bit-reproducible; no atomics).  More waves per workgroup means fewer
-// groups, and so fewer dependent memory round trips, per wave.
+// workgroup, and their fp32 sums meet in LDS and are added in wave order
+// (results are bit-reproducible; no atomics), after which every thread
+// stores part of the tile.  More waves per workgroup means fewer groups, and
+// so fewer dependent memory round trips, per wave.
 //
 // Matrix-core mapping.  Weights are the A operand (rows n), activations the B
 // operand (columns m), so a 16x16 output tile lands as 4 consecutive n for
 // one m in each lane.  Per 128-wide group:
 //   W4A8   2 x v_mfma_i32_16x16x64_i8 on (16*q_w, q_a) -> 16*P exactly, then
-//          acc += fp32(16*P) * (s_w / 16)      (exact scaling by 1/16)
+//          acc += fp32(16*P) * s_w; the token scale at the end carries the
+//          1/16 (a power of two: the same result as scaling each term)
 //   W4A16  4 x v_mfma_f32_16x16x32_f16 on exact fp16 codes q_w and fp16 x,
 //          then acc += group_sum * s_w
 //   W8A16  as W4A16 with int8 table codes converted exactly to fp16.
@@ -98,6 +100,7 @@ struct Stage;
 template <int NT, int MT>
 struct Stage<kW4A8, NT, MT> {
   uint4 w[NT];
+  uint2 sc[NT];     // the lane's 4 fp16 group scales per n-tile
   i32x4 x[MT][2];
 };
 
@@ -120,7 +123,7 @@ struct Stage<kW8A16, NT, MT> {
 // prefetch ring is branch-free and the compiler counts outstanding loads
 // exactly.
 struct Rsrc {
-  __amdgpu_buffer_rsrc_t w, x;
+  __amdgpu_buffer_rsrc_t w, s, x;
 };
 
 constexpr uint32_t kOOB = 0x80000000u;   // beyond every resource's extent (checked on the host)
@@ -146,8 +149,11 @@ __device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs
       st.w[j][0] = ld128(rs.w, row + bad);
       st.w[j][1] = ld128(rs.w, row + 64u + bad);
     } else {
+      // packed block (n-tile j, group g) and the lane's 4 scales of it
       const uint32_t blk = (uint32_t)j * G + (uint32_t)g;
       st.w[j] = ld128(rs.w, (blk * 64u + lane) * 16u + bad);
+      if constexpr (MODE == kW4A8)
+        st.sc[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.s, (blk * 16u + 4u * quad) * 2u + bad, 0, 0));
     }
   }
 #pragma unroll
@@ -168,8 +174,12 @@ __device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs
   }
 }
 
-// Group scales live in LDS as [group][column of the workgroup] fp16; a
-// stage past the wave's last group reads group 0's (its products are zero).
+// Group scales: W4A8 stages carry them (fp16, fed to v_fma_mix as they
+// are); W4A16 and W8A16 read them from LDS, stored there as [group][column
+// of the workgroup], where a stage past the wave's last group reads group
+// 0's (its products are zero).  W4A8 sums fp32(16 P) * s: the factor 16 of
+// the 16*q weights is removed with the token scale at the end (an exact
+// power of two, so the result is the same as scaling every term).
 template <int MODE, int NT, int MT, bool DEBUG>
 __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage<MODE, NT, MT>& st, int g,
                                               bool gvalid, int nt0, int lane, const uint16_t* lds_s,
@@ -178,23 +188,24 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
   const int gs = gvalid ? g : 0;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const uint2 sv = *reinterpret_cast<const uint2*>(lds_s + gs * (16 * NT) + j * 16 + 4 * quad);
-    float sc[4];
-    sc[0] = half_bits_to_float(sv.x & 0xFFFFu);
-    sc[1] = half_bits_to_float(sv.x >> 16);
-    sc[2] = half_bits_to_float(sv.y & 0xFFFFu);
-    sc[3] = half_bits_to_float(sv.y >> 16);
+    uint2 sv;
+    if constexpr (MODE == kW4A8)
+      sv = st.sc[j];
+    else
+      sv = *reinterpret_cast<const uint2*>(lds_s + gs * (16 * NT) + j * 16 + 4 * quad);
+    const _Float16 sc[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sv.x & 0xFFFFu)),
+                            __builtin_bit_cast(_Float16, (uint16_t)(sv.x >> 16)),
+                            __builtin_bit_cast(_Float16, (uint16_t)(sv.y & 0xFFFFu)),
+                            __builtin_bit_cast(_Float16, (uint16_t)(sv.y >> 16))};
     if constexpr (MODE == kW4A8) {
       const i32x4 a0 = w4_to_i8x16(st.w[j].x, st.w[j].y);
       const i32x4 a1 = w4_to_i8x16(st.w[j].z, st.w[j].w);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] *= 0.0625f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, st.x[mt][0], (i32x4)0, 0, 0, 0);
         P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, st.x[mt][1], P, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][mt][r] = fmaf((float)P[r], sc[r], acc[j][mt][r]);
+        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[r], (float)sc[r], acc[j][mt][r]);
         if constexpr (DEBUG) {
           const int m = mt * 16 + col;
           if (gvalid && m >= p.dm0 && m < p.dm1 && m < p.M) {
@@ -236,7 +247,7 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
         gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], b[2], gs, 0, 0, 0);
         gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], b[3], gs, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][mt][r] = fmaf(gs[r], sc[r], acc[j][mt][r]);
+        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(gs[r], (float)sc[r], acc[j][mt][r]);
       }
     }
   }
@@ -267,35 +278,41 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
       rs.x = make_rsrc(p.act, (uint32_t)((int64_t)((p.M + 15) / 16) * 16 * p.K));
     else
       rs.x = make_rsrc(p.act, (uint32_t)(((int64_t)(p.M - 1) * p.lda + p.K) * 2));
+    rs.s = make_rsrc(p.s + (int64_t)nt0 * G * 16, (uint32_t)(nvalid * G * 32));
   }
 
-  // The workgroup's group scales (NT*16 columns x G groups, one contiguous
-  // block in both scale layouts) go to LDS once, transposed to
-  // [group][column]; the loads are issued before the weight prefetch so the
-  // barrier below waits for them only.
+  // W4A16 / W8A16: the workgroup's group scales (NT*16 columns x G groups,
+  // one contiguous block in both scale layouts) go to LDS once, transposed
+  // to [group][column]; the loads are issued before the weight prefetch so
+  // the barrier below waits for them only.  (W4A8 stages carry their scales
+  // instead, one 8-byte load per n-tile and group: the decode kernel then
+  // starts multiplying as soon as its first stage lands.)
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_s[];
   constexpr int COLS = 16 * NT;
-  const int nsc = nvalid * 16 * p.G;           // scales of the valid columns
-  const uint16_t* sbase = MODE == kW8A16 ? p.s + (int64_t)nt0 * 16 * p.G : p.s + (int64_t)nt0 * p.G * 16;
   constexpr int SPT = 8;                       // scales per thread per pass (one 16-byte load)
   uint4 sreg[4];
-  const int npass = (nsc + 64 * NW * SPT - 1) / (64 * NW * SPT);
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(sbase, (uint32_t)nsc * 2u);
+  int nsc = 0, npass = 0;
+  const uint16_t* sbase = p.s + (int64_t)nt0 * 16 * p.G;   // same block start in both layouts
+  // scale index -> (column, group) in the block
+  auto scol = [&](int idx) { return MODE == kW8A16 ? idx / p.G : (idx / (16 * p.G)) * 16 + idx % 16; };
+  auto sgrp = [&](int idx) { return MODE == kW8A16 ? idx % p.G : (idx / 16) % p.G; };
+  if constexpr (MODE != kW4A8) {
+    nsc = nvalid * 16 * p.G;                   // scales of the valid columns
+    npass = (nsc + 64 * NW * SPT - 1) / (64 * NW * SPT);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(sbase, (uint32_t)nsc * 2u);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sreg[i] = ld128(srs, (uint32_t)(threadIdx.x + 64 * NW * i) * SPT * 2u);
-  for (int i = 4; i < npass; ++i) {            // very long K: load and store directly
-    const int e = (threadIdx.x + 64 * NW * i) * SPT;
-    if (e < nsc) {
-      const uint4 v = *reinterpret_cast<const uint4*>(sbase + e);
-      const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                             (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
+    for (int i = 0; i < 4; ++i) sreg[i] = ld128(srs, (uint32_t)(threadIdx.x + 64 * NW * i) * SPT * 2u);
+    for (int i = 4; i < npass; ++i) {          // very long K: load and store directly
+      const int e = (threadIdx.x + 64 * NW * i) * SPT;
+      if (e < nsc) {
+        const uint4 v = *reinterpret_cast<const uint4*>(sbase + e);
+        const uint16_t h[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
+                               (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int idx = e + t;
-        int c, g;
-        if constexpr (MODE == kW8A16) { c = idx / p.G; g = idx % p.G; }
-        else { c = (idx / (16 * p.G)) * 16 + idx % 16; g = (idx / 16) % p.G; }
-        lds_s[g * COLS + c] = h[t];
+        for (int t = 0; t < 8; ++t) {
+          const int idx = e + t;
+          lds_s[sgrp(idx) * COLS + scol(idx)] = h[t];
+        }
       }
     }
   }
@@ -318,24 +335,23 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
     load_stage<MODE, NT, MT>(p, rs, st[s], s < ng, gidx(s), lane);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (MODE != kW4A8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = (threadIdx.x + 64 * NW * i) * SPT;
-    if (i < npass && e < nsc) {
-      const uint16_t h[8] = {(uint16_t)sreg[i].x, (uint16_t)(sreg[i].x >> 16), (uint16_t)sreg[i].y,
-                             (uint16_t)(sreg[i].y >> 16), (uint16_t)sreg[i].z, (uint16_t)(sreg[i].z >> 16),
-                             (uint16_t)sreg[i].w, (uint16_t)(sreg[i].w >> 16)};
+    for (int i = 0; i < 4; ++i) {
+      const int e = (threadIdx.x + 64 * NW * i) * SPT;
+      if (i < npass && e < nsc) {
+        const uint16_t h[8] = {(uint16_t)sreg[i].x, (uint16_t)(sreg[i].x >> 16), (uint16_t)sreg[i].y,
+                               (uint16_t)(sreg[i].y >> 16), (uint16_t)sreg[i].z, (uint16_t)(sreg[i].z >> 16),
+                               (uint16_t)sreg[i].w, (uint16_t)(sreg[i].w >> 16)};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int idx = e + t;
-        int c, g;
-        if constexpr (MODE == kW8A16) { c = idx / p.G; g = idx % p.G; }
-        else { c = (idx / (16 * p.G)) * 16 + idx % 16; g = (idx / 16) % p.G; }
-        lds_s[g * COLS + c] = h[t];
+        for (int t = 0; t < 8; ++t) {
+          const int idx = e + t;
+          lds_s[sgrp(idx) * COLS + scol(idx)] = h[t];
+        }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   for (int r = 0; r + 1 < rounds; ++r) {
 #pragma unroll
@@ -356,51 +372,61 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
     }
   }
 
-  // Fixed-order tree sum over the waves: at each level the upper half of the
-  // remaining waves hands its sums to the lower half through LDS.
-  constexpr int E = NT * MT * 4;
-  if constexpr (NW > 1) {
-    __shared__ float red[NW / 2][E][64];
+  // Sum over the waves in wave order, QC (n-tile, m-tile) tiles at a time:
+  // every wave parks its f32x4 per lane and tile in LDS, one barrier, then
+  // thread t of a tile adds the 4 columns 4 (t % 4) .. + 3 of row t / 4 over
+  // the waves and stores them, so consecutive threads write consecutive
+  // bytes of a row.  Value (m, n) of a tile sits in lane m % 16 + 16 (n / 4),
+  // stored at slot lane ^ (lane / 16 % 4) so that the four lanes of a row
+  // fall in distinct LDS banks.  Two buffers alternate (one barrier per
+  // chunk); nothing is stored to global memory before the last barrier.
+  constexpr int Q = NT * MT;                                  // tiles per wave
+  constexpr int QC = Q * NW <= 32 ? Q : 32 / NW;              // tiles per chunk: <= 32 KiB per buffer
+  constexpr int NCH = (Q + QC - 1) / QC;
+  __shared__ f32x4 red[NCH > 1 ? 2 : 1][NW][QC][64];
+  const int tid = (int)threadIdx.x;
+  constexpr int KPC = (QC * 64 + 64 * NW - 1) / (64 * NW);     // sums per thread per chunk
+  f32x4 out[NCH][KPC];
 #pragma unroll
-    for (int half = NW / 2; half >= 1; half >>= 1) {
-      if (wave >= half && wave < 2 * half) {
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int b = NCH > 1 ? ch & 1 : 0;
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+    for (int qq = 0; qq < QC; ++qq) {
+      const int q = ch * QC + qq, j = q / MT, mt = q % MT;
+      if (q < Q) red[b][wave][qq][lane ^ ((lane >> 4) & 3)] = acc[j][mt];
+    }
+    __syncthreads();
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+    for (int k = 0; k < KPC; ++k) {
+      const int e = tid + 64 * NW * k;                        // (tile qq, row r, column quad c4)
+      out[ch][k] = (f32x4)0.0f;
+      if (e < QC * 64 && ch * QC + (e >> 6) < Q) {
+        const int qq = e >> 6, r = (e & 63) >> 2, c4 = e & 3;
+        const int l = r + 16 * c4;
+        f32x4 v = red[b][0][qq][l ^ c4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave - half][(j * MT + mt) * 4 + r][lane] = acc[j][mt][r];
+        for (int w = 1; w < NW; ++w) v += red[b][w][qq][l ^ c4];
+        out[ch][k] = v;
       }
-      __syncthreads();
-      if (wave < half) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][mt][r] += red[wave][(j * MT + mt) * 4 + r][lane];
-      }
-      if (half > 1) __syncthreads();
     }
   }
-  if (wave != 0) return;
-
-  const int col = lane & 15, quad = lane >> 4;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + col;
-    if (m >= p.M) continue;
-    const float ts = MODE == kW4A8 ? p.tok_scale[m] : 1.0f;
+  for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      if (j >= nvalid) continue;
-      const int n = (nt0 + j) * 16 + 4 * quad;
+    for (int k = 0; k < KPC; ++k) {
+      const int e = tid + 64 * NW * k;
+      if (e >= QC * 64 || ch * QC + (e >> 6) >= Q) continue;
+      const int q = ch * QC + (e >> 6), j = q / MT, mt = q % MT, r = (e & 63) >> 2, c4 = e & 3;
+      const int m = mt * 16 + r;
+      if (m >= p.M || j >= nvalid) continue;
+      // W4A8: token scale and the 1/16 of the 16*q weights
+      const float ts = MODE == kW4A8 ? p.tok_scale[m] * 0.0625f : 1.0f;
+      const f32x4 v = out[ch][k];
       uint2 o;
-      o.x = (uint32_t)float_to_half_bits(acc[j][mt][0] * ts) | ((uint32_t)float_to_half_bits(acc[j][mt][1] * ts) << 16);
-      o.y = (uint32_t)float_to_half_bits(acc[j][mt][2] * ts) | ((uint32_t)float_to_half_bits(acc[j][mt][3] * ts) << 16);
-      *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.N + n) = o;
+      o.x = (uint32_t)float_to_half_bits(v[0] * ts) | ((uint32_t)float_to_half_bits(v[1] * ts) << 16);
+      o.y = (uint32_t)float_to_half_bits(v[2] * ts) | ((uint32_t)float_to_half_bits(v[3] * ts) << 16);
+      *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.N + (nt0 + j) * 16 + 4 * c4) = o;
     }
-  }
 }
 
 // Prefetch depth: deep enough to keep several 1 KiB weight blocks per wave
@@ -413,7 +439,9 @@ constexpr int prefetch_depth() {
 template <int MODE, int NT, int NW, bool DEBUG>
 void launch_mt(const SkinnyParams& p, int mt, dim3 grid, hipStream_t st) {
   const dim3 block(64 * NW);
-  const size_t lds = (size_t)16 * NT * p.G * 2;   // the workgroup's group scales
+  // the workgroup's group scales (W4A16 / W8A16 only; K <= 65536 keeps
+  // this within 64 KiB)
+  const size_t lds = MODE == kW4A8 ? 0 : (size_t)16 * NT * p.G * 2;
   switch (mt) {
     case 1: skinny_kernel<MODE, NT, 1, NW, prefetch_depth<MODE, NT, 1>(), DEBUG><<<grid, block, lds, st>>>(p); break;
     case 2: skinny_kernel<MODE, NT, 2, NW, prefetch_depth<MODE, NT, 2>(), DEBUG><<<grid, block, lds, st>>>(p); break;

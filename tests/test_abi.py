@@ -81,6 +81,17 @@ def test_gemm_pointer_errors(name):
     assert call_gemm(name, M=0, x=None, w=None, s=None, y=None) == qg.QG_OK
 
 
+def test_fp16_activation_gemms_limit_k():
+    """w4a16_gemm / w8a16_gemm keep a workgroup's group scales in LDS, so K is
+    capped at 65536; W4A8 is not."""
+    K = 65536 + 128
+    assert call_gemm("w4a16_gemm", M=4, K=K, N=32) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert call_gemm("w8a16_gemm", M=4, K=K, N=32) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 4, K, 32) == 2 ** 64 - 1
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A16, 4, 65536, 32) == 0
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 4, K, 32) > 0
+
+
 def test_workspace_errors():
     need = qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 5120, 5120)
     assert call_gemm("w4a8_gemm", M=64, K=5120, N=5120, ws=None, wsb=0) == qg.QG_ERR_WORKSPACE

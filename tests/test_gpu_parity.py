@@ -138,7 +138,10 @@ def test_w4a8_prefill_workload_sampled(qg):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 16), (17, 256, 80), (33, 384, 144), (64, 1024, 48),
-                                   (65, 256, 144), (100, 512, 272), (129, 384, 128), (200, 128, 16)])
+                                   (65, 256, 144), (100, 512, 272), (129, 384, 128), (200, 128, 16),
+                                   # odd group counts per wave, ragged n-blocks, long K, wide N
+                                   (7, 2560, 176), (64, 4992, 400), (40, 17408, 96),
+                                   (5, 33024, 32), (4, 256, 16400)])
 def test_w4a8_ragged_shapes(qg, M, K, N):
     x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M + K)
     codes, scales = synth.weights(N, K, seed=N + K)
