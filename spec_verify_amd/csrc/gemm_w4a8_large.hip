@@ -8,20 +8,25 @@
 //
 // Tiling.  A workgroup of 4 wavefronts computes a 128 (m) x 128 (n) output
 // tile over all K; each wave owns a 64 x 64 quarter = 4 x 4 matrix-core
-// tiles of 16 x 16.  Per 128-wide group the workgroup stages the int8
-// activation codes (128 x 128 B, rows padded to 144 B so 16-byte LDS reads of
-// 16 consecutive rows hit distinct banks), the packed int4 weights (8 n-tiles
-// x 1 KiB, already in lane order) and the 128 group scales in LDS, double
-// buffered: the next group's buffer loads are issued before the current
-// group's matrix-core work and written to the other buffer after it.
+// tiles of 16 x 16.  Per 128-wide group the workgroup stages in LDS the int8
+// activation codes (128 rows x 128 B), the packed int4 weights (8 n-tiles x
+// 1 KiB, already in lane order) and the 128 group scales, double buffered,
+// with LDS-direct buffer loads: the data goes from memory straight into LDS
+// (16 B per lane at consecutive addresses), so staging takes no registers
+// and no LDS store instructions.  The next group's loads are issued before
+// the current group's matrix-core work; one barrier per group.
+//
+// Activation layout in LDS.  Row r holds its 8 16-byte parts at slots
+// part ^ ((r / 2) % 8), so the 16 rows a 16x16 tile's lanes read at one
+// part fall in 16 distinct groups of 4 banks.
 //
 // Rescale.  Per group and tile two v_mfma_i32_16x16x64_i8 give 16 * P
 // exactly; acc += fp32(16 P) * s (fp16 scale operand of v_fma_mix), and the
 // factor 1/16 joins the token scale in the epilogue.  That is two VALU
-// operations per output element per group, as much issue time as the
-// matrix-core work itself, so the two are software-pipelined: the 16 tiles
-// are split into two halves, and while one half's MFMAs run, the VALU
-// rescales the other half's previous partials.
+// operations per output element per group, about as much issue time as the
+// matrix-core work itself.  The kernel is sized for three workgroups per CU
+// (at most 168 VGPRs, 48.5 KiB of LDS), so three waves share each SIMD and
+// one wave's rescale runs beside another's matrix-core work.
 //
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin; ids are
 // remapped so each XCD walks a contiguous run of a grouped tile order (8
@@ -32,9 +37,8 @@
 namespace qg {
 namespace {
 
-constexpr int BM = 128, BN = 128, ASTR = 144, GROUP_M = 8;
+constexpr int BM = 128, BN = 128, GROUP_M = 8;
 constexpr uint32_t kHiNib = 0xF0F0F0F0u;
-constexpr uint32_t kOOB = 0x80000000u;
 
 struct LargeParams {
   const int8_t* codes;
@@ -48,38 +52,26 @@ struct LargeParams {
   int dm0, dm1, dn0, dn1;
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// voff: per-lane offset (fixed across the K loop); soff: wave-uniform offset
-// of the current group (kept in a scalar register).
-__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+// LDS-direct load: lane l's `size` bytes from rsrc + voff + soff land at
+// lds + size * l.  Out-of-range offsets store zeros.
+__device__ __forceinline__ void ld_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
-
-// acc[t] += fp32(P[t]) * scale, for the 8 tiles t of one half.
-__device__ __forceinline__ void rescale_half(f32x4 (&acc)[4][4], const i32x4 (&P)[8], const uint2 (&sc)[4], int h) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int j = 2 * h + t / 4, mt = t % 4;
-    const _Float16 s4[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sc[j].x & 0xFFFFu)),
-                            __builtin_bit_cast(_Float16, (uint16_t)(sc[j].x >> 16)),
-                            __builtin_bit_cast(_Float16, (uint16_t)(sc[j].y & 0xFFFFu)),
-                            __builtin_bit_cast(_Float16, (uint16_t)(sc[j].y >> 16))};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[t][r], (float)s4[r], acc[j][mt][r]);
-  }
+__device__ __forceinline__ void ld_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 4, voff, soff, 0, 0);
 }
 
 template <bool DEBUG>
-__global__ __launch_bounds__(256, 2) void w4a8_large_kernel(LargeParams p) {
-  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * ASTR];
+__global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
+  __shared__ __attribute__((aligned(16))) int8_t As[2][BM * 128];
   __shared__ __attribute__((aligned(16))) uint4 Bs[2][8 * 64];
-  // group scales: words 0..63 hold the 128 fp16 scales; every thread stores
-  // one word so the store needs no branch (words 64..255 take the zeros of
-  // out-of-range loads)
-  __shared__ __attribute__((aligned(16))) uint32_t Ss[2][256];
+  __shared__ __attribute__((aligned(16))) uint32_t Ss[2][64];   // 128 fp16 scales: [n-tile][16]
 
   // Tile of this workgroup (see "Placement").
   const int xcd = blockIdx.x & 7;
@@ -102,48 +94,33 @@ __global__ __launch_bounds__(256, 2) void w4a8_large_kernel(LargeParams p) {
   const int mrows = min(BM, p.M - m0);
   const int nvt = min(8, ntiles - nt_base);
 
-  // Range-checked resources: rows past M, n-tiles past N and the prefetch
-  // past the last group read zeros without touching memory.
+  // Range-checked resources: rows past M and n-tiles past N read zeros.
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.codes + (int64_t)m0 * p.K, (uint32_t)(mrows * (int64_t)p.K));
   const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.w + (int64_t)nt_base * G * 1024, (uint32_t)(nvt * (int64_t)G * 1024));
   const __amdgpu_buffer_rsrc_t rsS = make_rsrc(p.s + (int64_t)nt_base * G * 16, (uint32_t)(nvt * (int64_t)G * 32));
 
   // Per-lane offsets of the staging loads (the group adds a scalar offset).
-  uint32_t va[4], vb[2];
+  // A: wave w loads 1 KiB chunks c = 4w .. 4w+3 (rows 8c .. 8c+7); lane l
+  // fills row 8c + l/8, slot l%8 with part (l%8) ^ ((row/2) % 8).
+  uint32_t va[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    va[i] = (uint32_t)(c >> 3) * (uint32_t)p.K + 16u * (c & 7);
+    const int r = 8 * (4 * wave + i) + (lane >> 3);
+    va[i] = (uint32_t)r * (uint32_t)p.K + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
+  // B: wave w loads n-tiles 2w, 2w+1 (one 1 KiB block each).
+  uint32_t vb[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i;
-    vb[i] = ((uint32_t)(idx >> 6) * G * 64u + (idx & 63)) * 16u;
-  }
-  // scales of the 8 n-tiles: thread t < 64 loads rows 2(t&7), +1 of n-tile t>>3
-  const uint32_t vs = tid < 64 ? (((uint32_t)(tid >> 3) * G) * 16u + 2u * (tid & 7)) * 2u : kOOB;
+  for (int i = 0; i < 2; ++i) vb[i] = ((uint32_t)(2 * wave + i) * (uint32_t)G * 64u + lane) * 16u;
+  // S (wave 0): lane l loads scales 2(l%8), +1 of n-tile l/8.
+  const uint32_t vs = (((uint32_t)(lane >> 3) * (uint32_t)G) * 16u + 2u * (lane & 7)) * 2u;
 
-  uint4 ra[4], rb[2];
-  uint32_t rs;
-  auto gload = [&](int g, bool valid) {
-    const uint32_t sa = valid ? (uint32_t)g * kGroup : kOOB;
-    const uint32_t sb = valid ? (uint32_t)g * 1024u : kOOB;
-    const uint32_t ss = valid ? (uint32_t)g * 32u : kOOB;
+  auto gload = [&](int g, int8_t* A, uint4* B, uint32_t* S) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = ld128(rsA, va[i], sa);
+    for (int i = 0; i < 4; ++i) ld_lds16(rsA, A + (4 * wave + i) * 1024, va[i], (uint32_t)g * 128u);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) rb[i] = ld128(rsB, vb[i], sb);
-    rs = __builtin_amdgcn_raw_buffer_load_b32(rsS, vs, ss, 0);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, part = c & 7;
-      *reinterpret_cast<uint4*>(&As[buf][r * ASTR + 16 * part]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) Bs[buf][tid + 256 * i] = rb[i];
-    Ss[buf][tid] = rs;
+    for (int i = 0; i < 2; ++i) ld_lds16(rsB, B + (2 * wave + i) * 64, vb[i], (uint32_t)g * 1024u);
+    if (wave == 0) ld_lds4(rsS, S, vs, (uint32_t)g * 32u);
   };
 
   f32x4 acc[4][4];
@@ -152,74 +129,75 @@ __global__ __launch_bounds__(256, 2) void w4a8_large_kernel(LargeParams p) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[j][mt] = (f32x4)0.0f;
 
-  gload(0, true);
-  sstore(0);
+  // LDS byte offsets of this lane's activation operands: m-tile mt, half h
+  // (k 64h + 16 quad .. +15 of the group = part 4h + quad).
+  uint32_t xoff[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int rr = wm * 64 + mt * 16 + col;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) xoff[mt][h] = (uint32_t)rr * 128u + 16u * (uint32_t)((4 * h + quad) ^ ((rr >> 1) & 7));
+  }
+
+  gload(0, As[0], Bs[0], Ss[0]);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  i32x4 P[2][8];     // partials of the two halves of the wave's 16 tiles
-  uint2 sc[4], sc_prev[4];
   for (int g = 0; g < G; ++g) {
     const int buf = g & 1;
-    gload(g + 1, g + 1 < G);
-
-    i32x4 wa[4][2], xb[4][2];
+    // All of this group's operands come out of LDS first; only then are the
+    // next group's LDS-direct loads issued (into the other stage), so no
+    // LDS read of this group waits behind them.
+    i32x4 xb[4][2];
+    uint4 wv[4];
+    uint2 sv[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xb[mt][h] = *reinterpret_cast<const i32x4*>(&As[buf][xoff[mt][h]]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint4 w = Bs[buf][(wn * 4 + j) * 64 + lane];
-      wa[j][0][0] = (int32_t)((w.x << 4) & kHiNib); wa[j][0][1] = (int32_t)(w.x & kHiNib);
-      wa[j][0][2] = (int32_t)((w.y << 4) & kHiNib); wa[j][0][3] = (int32_t)(w.y & kHiNib);
-      wa[j][1][0] = (int32_t)((w.z << 4) & kHiNib); wa[j][1][1] = (int32_t)(w.z & kHiNib);
-      wa[j][1][2] = (int32_t)((w.w << 4) & kHiNib); wa[j][1][3] = (int32_t)(w.w & kHiNib);
-      sc[j] = *reinterpret_cast<const uint2*>(&Ss[buf][(wn * 4 + j) * 8 + 2 * quad]);
+      wv[j] = Bs[buf][(wn * 4 + j) * 64 + lane];
+      sv[j] = *reinterpret_cast<const uint2*>(&Ss[buf][(wn * 4 + j) * 8 + 2 * quad]);
     }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int8_t* src = &As[buf][(wm * 64 + mt * 16 + col) * ASTR + 16 * quad];
-      xb[mt][0] = *reinterpret_cast<const i32x4*>(src);
-      xb[mt][1] = *reinterpret_cast<const i32x4*>(src + 64);
-    }
+    if (g + 1 < G) gload(g + 1, As[buf ^ 1], Bs[buf ^ 1], Ss[buf ^ 1]);
 
-    // Half 0's MFMAs run beside the rescale of the previous group's half 1,
-    // half 1's beside the rescale of half 0 (the rescale of a half never
-    // waits for the matrix cores still working on the other half).
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int j = 0; j < 4; ++j) {
+      const uint4 w = wv[j];
+      i32x4 a0, a1;
+      a0[0] = (int32_t)((w.x << 4) & kHiNib); a0[1] = (int32_t)(w.x & kHiNib);
+      a0[2] = (int32_t)((w.y << 4) & kHiNib); a0[3] = (int32_t)(w.y & kHiNib);
+      a1[0] = (int32_t)((w.z << 4) & kHiNib); a1[1] = (int32_t)(w.z & kHiNib);
+      a1[2] = (int32_t)((w.w << 4) & kHiNib); a1[3] = (int32_t)(w.w & kHiNib);
+      const _Float16 s4[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sv[j].x & 0xFFFFu)),
+                              __builtin_bit_cast(_Float16, (uint16_t)(sv[j].x >> 16)),
+                              __builtin_bit_cast(_Float16, (uint16_t)(sv[j].y & 0xFFFFu)),
+                              __builtin_bit_cast(_Float16, (uint16_t)(sv[j].y >> 16))};
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        const int j = 2 * h + tt / 4, mt = tt % 4;
-        i32x4 v = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[j][0], xb[mt][0], (i32x4)0, 0, 0, 0);
-        P[h][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[j][1], xb[mt][1], v, 0, 0, 0);
-      }
-      if (h == 0) {
-        if (g > 0) rescale_half(acc, P[1], sc_prev, 1);
-      } else {
-        rescale_half(acc, P[0], sc, 0);
-      }
-    }
-    if constexpr (DEBUG) {
+      for (int mt = 0; mt < 4; ++mt) {
+        i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xb[mt][0], (i32x4)0, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, xb[mt][1], P, 0, 0, 0);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          const int j = 2 * h + tt / 4, mt = tt % 4;
+        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[r], (float)s4[r], acc[j][mt][r]);
+        if constexpr (DEBUG) {
           const int m = m0 + wm * 64 + mt * 16 + col;
           if (m >= p.dm0 && m < p.dm1 && m < p.M) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int n = (nt_base + wn * 4 + j) * 16 + 4 * quad + r;
               if (n >= p.dn0 && n < p.dn1 && n < p.N)
-                p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * G + g] = P[h][tt][r] >> 4;
+                p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * G + g] = P[r] >> 4;
             }
           }
         }
+      }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc_prev[j] = sc[j];
-
-    sstore(buf ^ 1);
+    // This wave's loads for group g + 1 have landed; after the barrier,
+    // every wave's have, and nobody reads this stage any more.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  if (G > 0) rescale_half(acc, P[1], sc_prev, 1);
 
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
