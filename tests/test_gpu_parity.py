@@ -80,8 +80,38 @@ def test_act_quant_edge_rows_and_strided_input(qg):
     assert np.array_equal(bits(host(s)), bits(os_))
 
 
+def test_act_quant_values_at_rounding_boundaries(qg):
+    """Every code boundary (k + 1/2) * scale, k = 0 .. 126, approached from
+    both sides and hit where fp16 can: the fp16 values nearest below, at and
+    above each boundary, both signs, for absmax values across the fp16
+    range (normal, large, tiny).  The kernel divides by multiplying with a
+    corrected reciprocal, so this is where it would differ from the IEEE
+    quotient."""
+    K = 1024
+    rows = []
+    for amax in (1.0, 3.0, 0.0107, 32752.0, 127.0, 6.103515625e-05, 1.1920929e-05):
+        a = np.float16(amax)
+        s = np.float32(np.float32(a) / np.float32(127.0))
+        vals = [a, -a]
+        for k in range(127):
+            t = np.float16(np.float32(k + 0.5) * s)
+            for v in (np.nextafter(t, np.float16(-np.inf)), t, np.nextafter(t, np.float16(np.inf))):
+                if abs(np.float32(v)) <= np.float32(a):
+                    vals += [v, -v]
+        row = np.zeros(K, np.float16)
+        row[:len(vals)] = np.array(vals, np.float16)[:K]
+        rows.append(row)
+    x = np.stack(rows)
+    assert all(np.abs(r.astype(np.float32)).max() == np.float32(np.float16(a)) for r, a in
+               zip(x, (1.0, 3.0, 0.0107, 32752.0, 127.0, 6.103515625e-05, 1.1920929e-05)))
+    q, s = qg.act_quant_int8(dev(x))
+    oq, os_ = oracle.quant_act(x)
+    assert np.array_equal(bits(host(s)), bits(os_))
+    assert np.array_equal(host(q), oq)
+
+
 def test_act_quant_long_rows_take_the_reload_path(qg):
-    x = synth.acts(3, 40960, 1.0, 0.01, 20.0, seed=10)   # longer than the register-resident chunk count
+    x = synth.acts(3, 66560, 1.0, 0.01, 20.0, seed=10)   # longer than 1024 threads x 8 register-resident chunks
     q, s = qg.act_quant_int8(dev(x))
     oq, os_ = oracle.quant_act(x)
     assert np.array_equal(host(q), oq)
