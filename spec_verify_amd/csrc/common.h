@@ -53,6 +53,13 @@ struct SkinnyArgs {
 };
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
 
+// Wide outputs with fp16 activations (W4A16 / W8A16, 32 < M <= 64): waves
+// split N and share each group's activations through LDS.  wide_waves gives
+// the waves per workgroup the kernel would use for this shape, 0 when the
+// weight-streaming kernel runs instead.
+int wide_waves(int mode, int64_t M, int64_t N);
+hipError_t launch_wide(const SkinnyArgs& a, hipStream_t st);
+
 struct LargeArgs {
   const int8_t* codes;      // [M][K]
   const float* tok_scale;   // [M]

@@ -31,6 +31,7 @@
 // in fragment order (see act_quant.hip): each 16-byte lane operand of a
 // 16-row m-tile is contiguous, so one load instruction moves 1 KiB.
 #include "common.h"
+#include "operands.h"
 
 namespace qg {
 namespace {
@@ -58,38 +59,6 @@ __device__ __forceinline__ i32x4 w4_to_i8x16(uint32_t w0, uint32_t w1) {
   r[2] = (int32_t)((w1 << 4) & kHiNib);
   r[3] = (int32_t)(w1 & kHiNib);
   return r;
-}
-
-// Exact fp16 values of the 8 int4 codes of one packed word.  With
-// u = nibble ^ 8 = q + 8, the pattern 0x6400 | u is the fp16 number 1024 + u
-// and 0x6400 | (u << 4) is 1024 + 16 u; so (v - 1032) and (v / 16 - 72) are
-// q exactly.  One shift by 8 serves slots 2, 3, 6, 7.  Element order is
-// slots {0, 4, 1, 5, 2, 6, 3, 7} = k offsets {0, 2, 4, 6, 1, 3, 5, 7} (the
-// activation operand is shuffled to match).
-__device__ __forceinline__ f16x8 w4_to_f16x8(uint32_t w) {
-  const uint32_t x = w ^ 0x88888888u;
-  const uint32_t y = x >> 8;
-  u32x4 p;
-  p[0] = (x & 0x000F000Fu) | 0x64006400u;
-  p[1] = (x & 0x00F000F0u) | 0x64006400u;
-  p[2] = (y & 0x000F000Fu) | 0x64006400u;
-  p[3] = (y & 0x00F000F0u) | 0x64006400u;
-  const f16x8 v = __builtin_bit_cast(f16x8, p);
-  const f16x8 mul = {1.0f16, 1.0f16, 0.0625f16, 0.0625f16, 1.0f16, 1.0f16, 0.0625f16, 0.0625f16};
-  const f16x8 add = {-1032.0f16, -1032.0f16, -72.0f16, -72.0f16, -1032.0f16, -1032.0f16, -72.0f16, -72.0f16};
-  return v * mul + add;
-}
-
-// Exact fp16 values of 8 int8 codes (natural order): byte b ^ 0x80 = b + 128
-// placed under exponent byte 0x64 is 1024 + b + 128.
-__device__ __forceinline__ f16x8 i8_to_f16x8(uint32_t w0, uint32_t w1) {
-  const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
-  u32x4 p;
-  p[0] = __builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u);
-  p[1] = __builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u);
-  p[2] = __builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u);
-  p[3] = __builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u);
-  return __builtin_bit_cast(f16x8, p) - (f16x8)(_Float16)1152.0f;
 }
 
 // One pipeline stage: one 128-wide group's weights and scales for the NT
@@ -480,6 +449,7 @@ SkinnyPlan skinny_plan(int mode, int64_t N, int64_t K) {
 
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
+  if (a.dbg == nullptr && wide_waves(a.mode, a.M, a.N) != 0) return launch_wide(a, st);
   SkinnyParams p;
   p.act = a.act;
   p.lda = a.lda;
