@@ -54,6 +54,30 @@ def gemm_bytes(M, K, N):
     return N * K // 2 + N * (K // 128) * 2 + M * K * 2 + M * N * 2
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_w4a8_m64_k5120_n5120_traffic.md")
+KERNEL_SOURCES = ["spec_verify_amd/csrc/gemm_skinny.hip", "spec_verify_amd/csrc/operands.h",
+                  "spec_verify_amd/csrc/common.h"]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode GEMM from the committed counter
+    passes (FETCH_SIZE and WRITE_SIZE, calibrated), or None when the kernel's
+    sources have changed since they were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and
+                      line.split(": ", 1)[0] in ("traffic_bytes_per_launch", "kernel_sources_sha256"))
+        if fields["kernel_sources_sha256"].split()[0] != h.hexdigest():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copies_for(nbytes):
     return max(2, -(-2 * MALL_BYTES // nbytes) + 1)
 
@@ -169,7 +193,7 @@ def main():
     achieved = kernel_bytes / (gemm_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", kernel="skinny_kernel<W4A8> (w4a8_gemm_prepared)", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
-                    bytes_per_launch=kernel_bytes, avg_launch_us=round(gemm_us, 3), traffic=None)
+                    bytes_per_launch=kernel_bytes, avg_launch_us=round(gemm_us, 3), traffic=measured_traffic())
 
     out = dict(metric=METRIC, value=round(value, 2), unit="GB/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_per_step, 6), higher_is_better=True, scaling="weak",
