@@ -216,9 +216,11 @@ def test_w4a16_verify_workload_full(qg, name):
 @pytest.mark.parametrize("M,K,N", [(1, 128, 16), (8, 5120, 80), (16, 384, 144), (64, 256, 48),
                                    (65, 256, 32), (150, 384, 96),
                                    # wide outputs (M > 32: waves split N, LDS-shared activations,
-                                   # 4 or 8 waves, a last workgroup with one valid n-tile; M <= 32:
+                                   # 4 or 8 waves of 2 n-tiles, or 8 waves of 4 n-tiles from 12288
+                                   # n-tiles on, a last workgroup with one valid n-tile; M <= 32:
                                    # the K-split kernel on many workgroups)
-                                   (5, 384, 32784), (33, 256, 32784), (64, 128, 131088), (3, 256, 131072)])
+                                   (5, 384, 32784), (33, 256, 32784), (64, 128, 131088), (3, 256, 131072),
+                                   (64, 128, 196624), (40, 256, 196608)])
 def test_w4a16_ragged_shapes(qg, M, K, N):
     x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M * 3 + K)
     codes, scales = synth.weights(N, K, seed=N * 3 + K)
@@ -251,7 +253,8 @@ def test_gather_bit_exact_with_out_of_range_ids(qg):
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 16), (64, 640, 400), (8, 256, 1040), (70, 256, 64),
                                    # wide outputs (see the W4A16 cases)
-                                   (40, 384, 32784), (9, 128, 131088), (64, 256, 32768), (48, 128, 131088)])
+                                   (40, 384, 32784), (9, 128, 131088), (64, 256, 32768), (48, 128, 131088),
+                                   (33, 256, 196624), (64, 128, 196624)])
 def test_w8a16_ragged_shapes(qg, M, K, N):
     src = synth.table_source(N, K, seed=N + 1)
     Q, S = oracle.quant_table(src)
