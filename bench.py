@@ -45,7 +45,29 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-workload extras")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB device copy that calibrates the FETCH_SIZE / WRITE_SIZE "
+                         "counters (run it under rocprofv3 --pmc), then exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB whose source is out of the caches
+    (filled, then a second 1 GiB buffer filled), three times, so that the
+    traffic counters can be scaled against bytes known to move."""
+    import torch
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    c = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    c.fill_(2)
+    for _ in range(3):
+        b.copy_(a)
+        c.fill_(3)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
 
 
 def gemm_bytes(M, K, N):
@@ -138,6 +160,9 @@ def main():
         print("bench.py measures one GPU: the path is single-GPU and no multi-GPU run is defined "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
