@@ -16,7 +16,9 @@ w4a8_gemm_prepared) against the 8 TB/s HBM peak.  `cpu_baseline` is the
 numpy oracle on the same workload on the host's cores.  `per_workload` adds
 the verify (W4A16, M = 8/16, N = 34816), prefill (W4A8, M = 4096, K = 17408)
 and vocabulary (int8 gather + lm_head over 248,320 rows) workloads measured
-the same way, for information.
+the same way, for information, and two lm_head variants: a 40,960-row draft
+head gathered from the int8 table (M = 1) and an int4 head over all 248,320
+rows (W4A16, M = 16 and 64).
 """
 from __future__ import annotations
 
@@ -280,6 +282,46 @@ def extras(torch, qg, synth, np, dev):
     res["lm_head_w8a16_m64"] = dict(M=cfg["M"], K=H, N=V, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
                                     frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4),
                                     TFLOPS=round(2 * cfg["M"] * V * H / us / 1e6, 2))
+
+    # lm_head variants: the 40,960-row draft head gathered once from the same
+    # table (copies rotated: 210 MB would otherwise stay in the Infinity Cache)
+    dcfg = synth.CONFIGS["draft_head_int8"]
+    D, Md = dcfg["D"], dcfg["M"]
+    dids = torch.from_numpy(synth.draft_ids(D, V, dcfg["seed"])).to(dev)
+    DQ, DS = Q.index_select(0, dids).contiguous(), S.index_select(0, dids).contiguous()
+    del Q, S, y
+    torch.cuda.empty_cache()
+    ncopy = copies_for(DQ.numel() + DS.numel() * 2)
+    dcopies = [(DQ, DS)] + [(DQ.clone(), DS.clone()) for _ in range(ncopy - 1)]
+    xd = torch.from_numpy(synth.acts(Md, H, dcfg["sigma"], dcfg["p"], dcfg["factor"], dcfg["seed"] + 100)).to(dev)
+    yd = torch.empty((Md, D), dtype=torch.float16, device=dev)
+    us, _ = graph_time_us(torch, lambda i: qg.w8a16_gemm(xd, dcopies[i % ncopy][0], dcopies[i % ncopy][1], y=yd),
+                          4 * ncopy, reps=2)
+    b = D * H + D * (H // 128) * 2 + Md * H * 2 + Md * D * 2
+    res["draft_head_w8a16_m1"] = dict(M=Md, K=H, N=D, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
+                                      frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), weight_copies=ncopy)
+    del dcopies, DQ, DS
+    torch.cuda.empty_cache()
+
+    # ... and an int4 head (W4A16 over all 248,320 rows), at verify and batch M
+    wcfg = synth.CONFIGS["lm_head_w4a16"]
+    K, N = wcfg["K"], wcfg["N"]
+    codes, scales = synth.weights(N, K, wcfg["seed"])
+    wp, sp = qg.w4_repack(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    del codes, scales
+    ncopy = copies_for(wp.numel() + sp.numel() * 2)
+    wcopies = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(ncopy - 1)]
+    for M in (16, wcfg["M"]):
+        xw = torch.from_numpy(synth.acts(M, K, wcfg["sigma"], wcfg["p"], wcfg["factor"], wcfg["seed"] + 100)).to(dev)
+        yw = torch.empty((M, N), dtype=torch.float16, device=dev)
+        us, _ = graph_time_us(torch, lambda i: qg.w4a16_gemm(xw, wcopies[i % ncopy][0], wcopies[i % ncopy][1], N,
+                                                             y=yw), 2 * ncopy, reps=2)
+        b = gemm_bytes(M, K, N)
+        res[f"lm_head_w4a16_m{M}"] = dict(M=M, K=K, N=N, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
+                                          frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                                          TFLOPS=round(2 * M * N * K / us / 1e6, 2), weight_copies=ncopy)
+    del wcopies, wp, sp
+    torch.cuda.empty_cache()
     return res
 
 

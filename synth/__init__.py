@@ -36,7 +36,7 @@ GROUP = 128
 CHUNK_ROWS = 1024
 
 # Stream ids keep the draws for different tensors of one seed independent.
-_S_CODES, _S_SMAG, _S_SSIGN, _S_ACT, _S_OUTL, _S_TABLE, _S_IDS = range(1, 8)
+_S_CODES, _S_SMAG, _S_SSIGN, _S_ACT, _S_OUTL, _S_TABLE, _S_IDS, _S_DRAFT = range(1, 9)
 
 _LOG_SMIN = float(np.log(1e-3))
 _LOG_SMAX = float(np.log(1e-2))
@@ -133,6 +133,12 @@ def token_ids(T: int, V: int, seed: int) -> np.ndarray:
     return _rng(seed, _S_IDS, 0).integers(0, V, size=T, dtype=np.int64).astype(np.int32)
 
 
+def draft_ids(D: int, V: int, seed: int) -> np.ndarray:
+    """A draft vocabulary: D distinct ids of [0, V), ascending, int64.  A
+    stand-in of the same size for a list counted over a model's outputs."""
+    return np.sort(_rng(seed, _S_DRAFT, 0).choice(V, size=D, replace=False)).astype(np.int64)
+
+
 # ---------------------------------------------------------------------------
 # The five workloads.  Seeds: weights use ``seed``, activations ``seed + 100``,
 # the vocabulary table ``seed + 200`` and token ids ``seed + 300``.
@@ -145,6 +151,11 @@ CONFIGS = {
     "prefill_w4a8": dict(op="w4a8", M=4096, K=17408, N=5120, sigma=0.5, p=0.005, factor=30.0, seed=3),
     "vocab_int8": dict(op="vocab", V=248320, H=5120, T=64, M=64, sigma=1.0, p=0.0, factor=1.0,
                        table_std=0.02, seed=4),
+    # lm_head variants: an int4 head (W4A16 over the 248,320 rows) and a
+    # 40,960-row draft head gathered once from the int8 table of vocab_int8
+    "lm_head_w4a16": dict(op="w4a16", M=64, K=5120, N=248320, sigma=1.0, p=0.0, factor=1.0, seed=5),
+    "draft_head_int8": dict(op="draft", V=248320, H=5120, D=40960, M=1, sigma=1.0, p=0.0, factor=1.0,
+                            table_std=0.02, seed=4),
 }
 
 

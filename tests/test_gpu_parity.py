@@ -288,7 +288,56 @@ def test_vocab_workload_full_table(qg):
     cols = np.unique(np.concatenate([rng.choice(V, 4096, replace=False), np.arange(V - 16, V)]))
     cQ, cS = oracle.quant_table(src[cols])
     assert_bounds(host(y)[:, cols], oracle.ref_w8a16(x, cQ, cS), "lm_head sampled columns")
-    del Qd, Sd, src
+
+    # the 40,960-row draft head: its rows gathered once from the table, then
+    # the same int8 lm_head product at M = 1 (sampled columns)
+    dcfg = synth.CONFIGS["draft_head_int8"]
+    dids = synth.draft_ids(dcfg["D"], V, dcfg["seed"])
+    dt = torch.from_numpy(dids).to(DEV)
+    DQ, DS = Qd.index_select(0, dt).contiguous(), Sd.index_select(0, dt).contiguous()
+    xd = synth.acts(dcfg["M"], H, dcfg["sigma"], dcfg["p"], dcfg["factor"], dcfg["seed"] + 100)
+    yd = qg.w8a16_gemm(dev(xd), DQ, DS)
+    dcols = np.unique(np.concatenate([rng.choice(dcfg["D"], 2048, replace=False), np.arange(dcfg["D"] - 8, dcfg["D"])]))
+    dQ, dS = oracle.quant_table(src[dids[dcols]])
+    assert_bounds(host(yd)[:, dcols], oracle.ref_w8a16(xd, dQ, dS), "draft head sampled columns")
+    del Qd, Sd, DQ, DS, src
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_draft_head_is_the_lm_head_over_a_row_subset(qg, M):
+    """A draft head of 40,960 distinct rows gathered from a requantised table:
+    the gathered rows are the table's rows bit for bit, and the product over
+    them matches the oracle's over the same rows (every column)."""
+    V, H = 60000, 1280
+    src = synth.table_source(V, H, seed=41)
+    Qd, Sd = qg.quant_table_int8(dev(src.view(np.int16)))
+    oQ, oS = oracle.quant_table(src)
+    ids = synth.draft_ids(40960, V, seed=41)
+    dt = torch.from_numpy(ids).to(DEV)
+    DQ, DS = Qd.index_select(0, dt).contiguous(), Sd.index_select(0, dt).contiguous()
+    assert np.array_equal(host(DQ), oQ[ids])
+    assert np.array_equal(bits(host(DS)), bits(oS[ids]))
+    x = synth.acts(M, H, 1.0, 0.0, 1.0, seed=M + 42)
+    y = qg.w8a16_gemm(dev(x), DQ, DS)
+    assert_bounds(host(y), oracle.ref_w8a16(x, oQ[ids], oS[ids]), "draft head")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [16, 64])
+def test_int4_lm_head_full_size(qg, M):
+    """An int4 lm_head over all 248,320 rows (W4A16, group-128 signed scales):
+    M = 16 takes the K-split kernel, M = 64 the wide-output one (sampled
+    columns, the last tiles included)."""
+    cfg = synth.CONFIGS["lm_head_w4a16"]
+    K, N = cfg["K"], cfg["N"]
+    codes, scales = synth.weights(N, K, cfg["seed"])
+    wp, sp = packed(qg, codes, scales)
+    x = synth.acts(M, K, cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)
+    y = host(qg.w4a16_gemm(dev(x), wp, sp, N))
+    rng = np.random.default_rng(M)
+    cols = np.unique(np.concatenate([rng.choice(N, 4096, replace=False), np.arange(N - 16, N)]))
+    assert_bounds(y[:, cols], oracle.ref_w4a16(x, codes[cols], scales[cols]), f"int4 lm_head M={M}")
+    del wp, sp
 
 
 # ---------------------------------------------------------------------------

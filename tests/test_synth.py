@@ -44,3 +44,11 @@ def test_generation_is_deterministic_and_independent_of_threads(monkeypatch):
 def test_token_ids_in_range():
     ids = synth.token_ids(64, 248320, seed=304)
     assert ids.dtype == np.int32 and ids.min() >= 0 and ids.max() < 248320
+
+
+def test_draft_ids_are_distinct_sorted_and_seeded():
+    ids = synth.draft_ids(40960, 248320, seed=4)
+    assert ids.shape == (40960,) and ids.dtype == np.int64
+    assert ids.min() >= 0 and ids.max() < 248320
+    assert np.all(np.diff(ids) > 0)
+    assert np.array_equal(ids, synth.draft_ids(40960, 248320, seed=4))
