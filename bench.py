@@ -18,7 +18,8 @@ the verify (W4A16, M = 8/16, N = 34816), prefill (W4A8, M = 4096, K = 17408)
 and vocabulary (int8 gather + lm_head over 248,320 rows) workloads measured
 the same way, for information, and two lm_head variants: a 40,960-row draft
 head gathered from the int8 table (M = 1) and an int4 head over all 248,320
-rows (W4A16, M = 16 and 64).
+rows (W4A16, M = 16 and 64); and the RMSNorm fused with the W4A8 quantiser
+at the decode and prefill shapes.
 """
 from __future__ import annotations
 
@@ -264,6 +265,21 @@ def extras(torch, qg, synth, np, dev):
                          frac_mfma=round(ops / us / 1e6 / peak_ops, 4), weight_copies=ncopy)
         del copies, wp, sp
         torch.cuda.empty_cache()
+
+    # the quantiser fused into the norm that makes its input (one launch per
+    # hidden state; the prepared buffer then feeds every W4A8 GEMM of it)
+    for name in ("decode_w4a8", "prefill_w4a8"):
+        cfg = synth.CONFIGS[name]
+        M, H = cfg["M"], cfg["K"]
+        x = torch.from_numpy(synth.acts(M, H, cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)).to(dev)
+        wn = torch.from_numpy(synth.acts(1, H, 0.1, 0.0, 1.0, cfg["seed"] + 400)[0]).to(dev)
+        prep = torch.empty((qg.w4a8_prepared_bytes(M, H),), dtype=torch.uint8, device=dev)
+        yn = torch.empty((M, H), dtype=torch.float16, device=dev)
+        us, _ = graph_time_us(torch, lambda i: qg.rmsnorm_w4a8_prepare(x, wn, 1e-6, prepared=prep, y=yn), 20, reps=5)
+        b = M * H * 2 + H * 2 + M * H * 2 + M * H + M * 4      # x, w in; y, codes, token scales out
+        res[f"rmsnorm_w4a8_prepare_m{M}"] = dict(M=M, H=H, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
+                                                 frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
+        del x, prep, yn
 
     cfg = synth.CONFIGS["vocab_int8"]
     V, H = cfg["V"], cfg["H"]

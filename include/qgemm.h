@@ -153,6 +153,30 @@ int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, co
                        const void* s_packed, void* y_f16, void* stream);
 
 /*
+ * rmsnorm_w4a8_prepare -- the quantiser fused into the norm that produces
+ * the GEMM's input, so the activations are quantised once, where they are
+ * made, and the prepared buffer feeds every W4A8 GEMM of that hidden state
+ * ([OPT] "In full" item 4: activations are quantised to int8 per token; the
+ * pages name no norm, so the norm below is a plain reading).
+ *   x         fp16 [M][ldx] (first H columns used), ldx >= H, ldx % 8 == 0
+ *   w         fp16 [H], the norm's weight
+ *   eps       >= 0, finite
+ *   y         fp16 [M][H] out, contiguous, or NULL to skip it
+ *             y[m][h] = fp16((fp32(x[m][h]) * r[m]) * fp32(w[h])), with
+ *             r[m] = 1 / sqrt(ss[m] / H + eps) in IEEE fp32 (division, square
+ *             root, division; r = 0 where ss / H + eps == 0) and ss[m] the
+ *             fp32 sum of x[m][h]^2 as a binary tree over the row zero-padded
+ *             to a power of two (adjacent entries pairwise, level by level)
+ *   prepared  out, prepared_bytes >= w4a8_prepared_bytes(M, H): exactly what
+ *             w4a8_prepare writes for y (codes and token scales of
+ *             act_quant_int8 on y), for w4a8_gemm_prepared with K = H
+ *   H % 128 == 0, H <= 65536.  y and the codes are bit-exact against that
+ *   definition.  One kernel launch.
+ */
+int rmsnorm_w4a8_prepare(const void* x_f16, const void* w_f16, int64_t M, int64_t H, int64_t ldx, float eps,
+                         void* y_f16, void* prepared, size_t prepared_bytes, void* stream);
+
+/*
  * w4a8_gemm_debug -- w4a8_gemm that also exposes its integer stages, for
  * bit-exact checks.  Runs the same kernels as w4a8_gemm and in addition
  * writes

@@ -30,8 +30,11 @@ is exact (the oracle does not round q*s to fp16); out-of-range token ids give
 zero rows.
 
 Parity pins: every function below is pinned in ``tests/test_oracle_*.py`` by
-brute force with exact rationals, closed forms and invariants; none is
-"parity unpinned".
+brute force with exact rationals, closed forms and invariants.  One step has
+no page behind it: ``rmsnorm`` (the norm whose output the fused quantiser
+takes; the pages name no norm).  Its definition is a reading, pinned by
+closed forms, an exact scale invariance and a float64 bound, and is marked
+"parity unpinned" as to the pages.
 """
 from __future__ import annotations
 
@@ -42,6 +45,7 @@ GROUP = 128
 __all__ = [
     "GROUP", "quant_act", "partials", "ref_w4a8", "ref_w4a16", "quant_table",
     "ref_gather", "ref_w8a16", "fp16_bounds", "FP16_MAX_RATIO", "FP16_FROB",
+    "tree_sum_f32", "rmsnorm_factor", "rmsnorm_f32", "rmsnorm", "rmsnorm_quant",
 ]
 
 # Tolerance for fp16 outputs against the float64 reference:
@@ -74,6 +78,69 @@ def quant_act(x):
         quot = xf[nz] / s[nz][:, None]            # float32 / float32: IEEE
         q[nz] = np.clip(np.rint(quot), -127, 127).astype(np.int8)
     return q, s
+
+
+def tree_sum_f32(v):
+    """Row sums of a float32 matrix as a binary tree: the row is zero-padded
+    to a power-of-two length, then adjacent entries are added pairwise,
+    level by level, in float32.  (Padding further only adds zero subtrees,
+    which leave every sum unchanged, so the power chosen does not matter.)"""
+    v = np.asarray(v, dtype=np.float32)
+    M, n = v.shape
+    p = 1
+    while p < n:
+        p *= 2
+    t = np.zeros((M, p), np.float32)
+    t[:, :n] = v
+    while t.shape[1] > 1:
+        t = t[:, 0::2] + t[:, 1::2]
+    return t[:, 0]
+
+
+def rmsnorm_factor(x, eps):
+    """The per-row factor r of ``rmsnorm`` (float32 [M]): for row m of length H
+        ss[m] = tree_sum_f32(fp32(x[m, :]) ** 2)   (each square is exact)
+        t[m]  = ss[m] / H + eps                    (IEEE fp32 division, then add)
+        r[m]  = 1 / sqrt(t[m])                     (IEEE fp32 sqrt, then division)
+    and r = 0 for a row with t == 0 (all zeros, eps == 0)."""
+    xf = np.asarray(x, dtype=np.float16).astype(np.float32)
+    M, H = xf.shape
+    r = np.zeros(M, np.float32)
+    if M == 0:
+        return r
+    ss = tree_sum_f32(xf * xf)
+    t = ss / np.float32(H) + np.float32(eps)
+    pos = t > 0
+    r[pos] = np.float32(1.0) / np.sqrt(t[pos])
+    return r
+
+
+def rmsnorm_f32(x, w, eps):
+    """The float32 values rmsnorm rounds to fp16: (fp32(x[m, h]) * r[m]) * fp32(w[h])."""
+    xf = np.asarray(x, dtype=np.float16).astype(np.float32)
+    wf = np.asarray(w, dtype=np.float16).astype(np.float32)
+    r = rmsnorm_factor(x, eps)
+    return (xf * r[:, None]) * wf[None, :]
+
+
+def rmsnorm(x, w, eps):
+    """RMSNorm of fp16 rows with an fp16 weight, all in float32.
+
+    Parity unpinned as to the pages, which name no norm: this is the plain
+    reading of the norm whose output a fused quantiser would take.
+        y[m, h] = fp16((fp32(x[m, h]) * r[m]) * fp32(w[h]))
+    with r from ``rmsnorm_factor`` (a root-mean-square over the row, by a
+    float32 binary-tree sum).  Returns y as float16 [M, H].
+    """
+    return rmsnorm_f32(x, w, eps).astype(np.float16)
+
+
+def rmsnorm_quant(x, w, eps):
+    """The fused normalise-and-quantise step: y = rmsnorm(x, w, eps), then the
+    per-token int8 quantisation of y.  Returns (y fp16, q int8, s float32)."""
+    y = rmsnorm(x, w, eps)
+    q, s = quant_act(y)
+    return y, q, s
 
 
 def partials(q, codes):

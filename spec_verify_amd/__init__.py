@@ -7,7 +7,7 @@ torch stream.  All arithmetic runs in the library's HIP kernels.  If the
 library has not been built the import fails; there is no fallback.
 
 Entry points (see ``include/qgemm.h`` for the contract of each):
-act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare,
+act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare, rmsnorm_w4a8_prepare,
 w4a8_gemm_prepared, w4a8_gemm_debug,
 w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, plus the size
 helpers w4_packed_bytes, w4_scales_bytes, qg_workspace_bytes and
@@ -52,6 +52,7 @@ _SIGS = {
     "w4a8_gemm": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "w4a8_prepared_bytes": (_sz, [_i64, _i64]),
     "w4a8_prepare": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _sz, _p]),
+    "rmsnorm_w4a8_prepare": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _sz, _p]),
     "w4a8_gemm_prepared": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "w4a8_gemm_debug": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p,
                                        _p, _p, _p, _i64, _i64, _i64, _i64]),
@@ -182,6 +183,22 @@ def w4a8_prepare(x, prepared=None):
     _check("w4a8_prepare", lib.w4a8_prepare(_ptr(x), M, K, _ldx(x), _ptr(prepared),
                                             prepared.numel() * prepared.element_size(), _stream(x.device)))
     return prepared
+
+
+def rmsnorm_w4a8_prepare(x, w, eps, prepared=None, y=None, want_y=True):
+    """RMSNorm of x [M, H] with weight w [H], fused with the W4A8 quantiser:
+    returns (y fp16 [M, H] or None, prepared) where prepared is what
+    w4a8_prepare(y) would write."""
+    import torch
+    M, H = x.shape
+    need = w4a8_prepared_bytes(M, H)
+    prepared = _empty((max(1, need),), torch.uint8, x) if prepared is None else prepared
+    if want_y and y is None:
+        y = _empty((M, H), torch.float16, x)
+    _check("rmsnorm_w4a8_prepare",
+           lib.rmsnorm_w4a8_prepare(_ptr(x), _ptr(w), M, H, _ldx(x), float(eps), _ptr(y) if want_y else None,
+                                    _ptr(prepared), prepared.numel() * prepared.element_size(), _stream(x.device)))
+    return (y if want_y else None), prepared
 
 
 def w4a8_gemm_prepared(prepared, M, K, w_packed, s_packed, N, y=None):

@@ -64,6 +64,19 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float rs) {
   return make_uint2(out[0], out[1]);
 }
 
+// Stores the 8 codes of chunk c (k = 8c .. 8c+7) of row m in the requested
+// orders: row-major q (if q) and/or the fragment order (if qfrag).
+__device__ __forceinline__ void put_codes(int8_t* q, int64_t ldq, int8_t* qfrag, int64_t m, int G, int c,
+                                          uint2 codes) {
+  if (q) *reinterpret_cast<uint2*>(q + m * ldq + 8 * c) = codes;
+  if (qfrag) {
+    const int mt = (int)(m >> 4), col = (int)(m & 15);
+    const int k = 8 * c, g = k >> 7, kk = k & 127, h = kk >> 6, quad = (kk & 63) >> 4;
+    const int64_t off = ((((int64_t)mt * G + g) * 2 + h) * 64 + col + 16 * quad) * 16 + (kk & 15);
+    *reinterpret_cast<uint2*>(qfrag + off) = codes;
+  }
+}
+
 // The workgroup's blockDim.x threads cooperate on one row; each holds up to
 // MAXC 16-byte chunks (8 fp16 values) in registers.  Chunks past
 // blockDim.x * MAXC are re-read from memory in the quantise pass (only for
@@ -105,16 +118,7 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(const uint16_t* __restr
   const float rs = 1.0f / s;    // IEEE fp32 division, once per thread
   if (t == 0) scale[m] = a > 0.0f ? s : 0.0f;
   const int G = K / kGroup;
-  const int mt = (int)(m >> 4), col = (int)(m & 15);
-  // stores the 8 codes of chunk c (k = 8c .. 8c+7) in the requested orders
-  auto put = [&](int c, uint2 codes) {
-    if (q) *reinterpret_cast<uint2*>(q + m * ldq + 8 * c) = codes;
-    if (qfrag) {
-      const int k = 8 * c, g = k >> 7, kk = k & 127, h = kk >> 6, quad = (kk & 63) >> 4;
-      const int64_t off = ((((int64_t)mt * G + g) * 2 + h) * 64 + col + 16 * quad) * 16 + (kk & 15);
-      *reinterpret_cast<uint2*>(qfrag + off) = codes;
-    }
-  };
+  auto put = [&](int c, uint2 codes) { put_codes(q, ldq, qfrag, m, G, c, codes); };
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int c = t + T * i;
@@ -124,7 +128,177 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(const uint16_t* __restr
     put(c, a > 0.0f ? quant8(*reinterpret_cast<const uint4*>(row + 8 * c), s, rs) : make_uint2(0, 0));
 }
 
+// ---------------------------------------------------------------------------
+// RMSNorm fused with the quantiser: the norm's fp16 output y is quantised per
+// row exactly as above (its codes and scale are those of act_quant on y).
+//
+// The norm, per row of length H, all in fp32:
+//   ss = sum of x[h]^2 as a binary tree over the row zero-padded to a power
+//        of two (adjacent entries pairwise, level by level; squares of fp16
+//        values are exact in fp32, and adding zero subtrees changes nothing)
+//   r  = 1 / sqrt(ss / H + eps)   (IEEE division, square root, division;
+//        r = 0 when ss / H + eps == 0)
+//   y  = fp16((x * r) * w)
+// The tree is formed by the thread layout: chunk c (8 values, itself summed as
+// a 3-level tree) belongs to thread c % T in slot c / T; lanes then add by
+// xor-shuffles (aligned blocks of 2, 4, .., 64 lanes), waves pairwise
+// through LDS, and finally the MAXC slots pairwise.  T and MAXC are powers
+// of two with T * MAXC chunks >= the row.
+// ---------------------------------------------------------------------------
+
+// Sum over a wave's lanes as a balanced binary tree over lane index: after
+// the step with offset o every lane holds the sum of its aligned block of 2o
+// lanes (fp32 addition is commutative, so both lanes of a pair agree).
+__device__ __forceinline__ float wave_tree_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = v + __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Pairwise tree over n (a power of two) consecutive values, in place; returns a[0].
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&a)[N]) {
+#pragma unroll
+  for (int s = 1; s < N; s <<= 1)
+#pragma unroll
+    for (int j = 0; j + s < N; j += 2 * s) a[j] = a[j] + a[j + s];
+  return a[0];
+}
+
+// Squares of 8 fp16 values summed as ((e0+e1)+(e2+e3))+((e4+e5)+(e6+e7)).
+__device__ __forceinline__ float sumsq8(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = half_bits_to_float(w[i] & 0xFFFFu), b = half_bits_to_float(w[i] >> 16);
+    e[2 * i] = a * a;
+    e[2 * i + 1] = b * b;
+  }
+  return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+}
+
+// fp16((x * r) * w) for 8 values: the product rounded to fp32, then to fp16.
+// The empty asm makes the fp32 product a value of its own: otherwise the
+// compiler fuses the second product and the conversion into one
+// mixed-precision multiply that rounds once, straight to fp16, which
+// differs from the two roundings where the fp32 product is a tie.
+__device__ __forceinline__ uint4 norm8(uint4 xv, uint4 wv, float r) {
+  const uint32_t xs[4] = {xv.x, xv.y, xv.z, xv.w}, ws[4] = {wv.x, wv.y, wv.z, wv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = (half_bits_to_float(xs[i] & 0xFFFFu) * r) * half_bits_to_float(ws[i] & 0xFFFFu);
+    float hi = (half_bits_to_float(xs[i] >> 16) * r) * half_bits_to_float(ws[i] >> 16);
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    o[i] = (uint32_t)float_to_half_bits(lo) | ((uint32_t)float_to_half_bits(hi) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int T, int MAXC>
+__global__ __launch_bounds__(T) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int H,
+                                                          const uint16_t* __restrict__ w, float eps,
+                                                          uint16_t* __restrict__ y, int8_t* __restrict__ q,
+                                                          int64_t ldq, int8_t* __restrict__ qfrag,
+                                                          float* __restrict__ scale) {
+  constexpr int NWV = T / kWave;
+  const int t = (int)threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+  const int64_t m = blockIdx.x;
+  const uint16_t* row = x + m * ldx;
+  const int nch = H >> 3;
+
+  uint4 xv[MAXC], wvec[MAXC];
+  float part[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = t + T * i;
+    if (c < nch) {
+      xv[i] = *reinterpret_cast<const uint4*>(row + 8 * c);
+      wvec[i] = *reinterpret_cast<const uint4*>(w + 8 * c);
+      part[i] = sumsq8(xv[i]);
+    } else {
+      xv[i] = wvec[i] = make_uint4(0, 0, 0, 0);
+      part[i] = 0.0f;
+    }
+  }
+
+  // slot i over the T threads: lanes, then waves; then the slots
+  __shared__ float wsum[MAXC][NWV];
+  __shared__ float wmax[NWV];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const float v = wave_tree_sum(part[i]);
+    if (lane == 0) wsum[i][wv] = v;
+  }
+  __syncthreads();
+  float slot[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    float a[NWV];
+#pragma unroll
+    for (int j = 0; j < NWV; ++j) a[j] = wsum[i][j];
+    slot[i] = tree_sum(a);
+  }
+  const float ss = tree_sum(slot);
+  const float tt = ss / (float)H + eps;                 // IEEE division, then add
+  const float r = tt > 0.0f ? 1.0f / sqrtf(tt) : 0.0f;  // IEEE square root and division
+
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = t + T * i;
+    if (c < nch) {
+      xv[i] = norm8(xv[i], wvec[i], r);                 // xv now holds y
+      if (y) *reinterpret_cast<uint4*>(y + m * (int64_t)H + 8 * c) = xv[i];
+      amax = max(amax, absmax_bits8(xv[i]));
+    }
+  }
+  float a = wave_max(half_bits_to_float(amax));
+  if (NWV > 1) {
+    if (lane == 0) wmax[wv] = a;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NWV; ++j) a = fmaxf(a, wmax[j]);
+  }
+
+  const float s = a / 127.0f;   // as act_quant_kernel
+  const float rs = 1.0f / s;
+  if (t == 0) scale[m] = a > 0.0f ? s : 0.0f;
+  const int G = H / kGroup;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = t + T * i;
+    if (c < nch) put_codes(q, ldq, qfrag, m, G, c, a > 0.0f ? quant8(xv[i], s, rs) : make_uint2(0, 0));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, int64_t ldx, float eps,
+                                uint16_t* y, int8_t* q, int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const int64_t nch = H / 8;
+  int64_t p = 1;
+  while (p < nch) p *= 2;                         // chunks of the padded row
+  const dim3 grid((unsigned)M);
+  const int64_t threads = std::min<int64_t>(1024, std::max<int64_t>(64, p));
+  const int64_t maxc = std::max<int64_t>(1, p / threads);
+#define QG_RMS(TH, MC) rmsnorm_quant_kernel<TH, MC><<<grid, dim3(TH), 0, st>>>(x, ldx, (int)H, w, eps, y, q, ldq, qfrag, scale)
+  switch (threads * 16 + maxc) {
+    case 64 * 16 + 1: QG_RMS(64, 1); break;
+    case 128 * 16 + 1: QG_RMS(128, 1); break;
+    case 256 * 16 + 1: QG_RMS(256, 1); break;
+    case 512 * 16 + 1: QG_RMS(512, 1); break;
+    case 1024 * 16 + 1: QG_RMS(1024, 1); break;
+    case 1024 * 16 + 2: QG_RMS(1024, 2); break;
+    case 1024 * 16 + 4: QG_RMS(1024, 4); break;
+    case 1024 * 16 + 8: QG_RMS(1024, 8); break;
+    default: return hipErrorInvalidValue;         // rows longer than 65536 (rejected on the host)
+  }
+#undef QG_RMS
+  return hipGetLastError();
+}
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                             int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st) {

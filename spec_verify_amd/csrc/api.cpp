@@ -1,6 +1,7 @@
 // C-ABI entry points of libqgemm: host-side validation, workspace layout and
 // dispatch to the gfx950 kernels.  Nothing here allocates device memory or
 // synchronises the host; every check happens before the first launch.
+#include <cmath>
 #include "qgemm.h"
 
 #include <stdint.h>
@@ -289,6 +290,29 @@ int w4a8_prepare(const void* x_f16, int64_t M, int64_t K, int64_t ldx, void* pre
   if (prepared_bytes < w4a8_layout(M, K).total) return QG_ERR_WORKSPACE;
   clear_stale_error();
   return prepare_impl(x_f16, M, K, ldx, prepared, nullptr, as_stream(stream));
+}
+
+int rmsnorm_w4a8_prepare(const void* x_f16, const void* w_f16, int64_t M, int64_t H, int64_t ldx, float eps,
+                         void* y_f16, void* prepared, size_t prepared_bytes, void* stream) {
+  int st = check_w4a8_shape(M, H, 16);
+  if (st != QG_OK) return st;
+  if (H > kMaxK16) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (ldx < H || ldx % 8 != 0 || !(eps >= 0.0f) || !std::isfinite(eps)) return QG_ERR_INVALID_ARG;
+  if (M == 0) return QG_OK;
+  if (!x_f16 || !w_f16 || !prepared || !aligned16(x_f16) || !aligned16(w_f16) || !aligned16(prepared) ||
+      (y_f16 && !aligned16(y_f16)))
+    return QG_ERR_INVALID_ARG;
+  if (prepared_bytes < w4a8_layout(M, H).total) return QG_ERR_WORKSPACE;
+  const W4A8Layout L = w4a8_layout(M, H);
+  char* base = reinterpret_cast<char*>(prepared);
+  int8_t* q = reinterpret_cast<int8_t*>(base + L.q_off);
+  float* ts = reinterpret_cast<float*>(base + L.s_off);
+  const bool skinny = M <= kSkinnyMaxM;
+  clear_stale_error();
+  return launch_status(qg::launch_rmsnorm_quant(reinterpret_cast<const uint16_t*>(x_f16),
+                                                reinterpret_cast<const uint16_t*>(w_f16), M, H, ldx, eps,
+                                                reinterpret_cast<uint16_t*>(y_f16), skinny ? nullptr : q, H,
+                                                skinny ? q : nullptr, ts, as_stream(stream)));
 }
 
 int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, const void* w_packed,

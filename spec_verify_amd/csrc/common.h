@@ -25,6 +25,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // weight-streaming W4A8 kernel reads when qfrag is not null.
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             int8_t* q, int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st);
+// RMSNorm of fp16 rows with an fp16 weight (fp32 math, tree-ordered sum of
+// squares), optionally written to y ([M][H]), then quantised exactly as by
+// launch_act_quant.  H % 128 == 0, H <= 65536.
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, int64_t ldx, float eps,
+                                uint16_t* y, int8_t* q, int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st);
 
 hipError_t launch_w4_repack(const int8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                             void* w_packed, uint16_t* s_packed, hipStream_t st);

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(qg.lib, n), n
     assert set(names) == set(qg.EXPORTS)
@@ -128,3 +128,25 @@ def test_quantiser_repack_gather_table_errors():
     assert L.embed_gather_dequant_int8(None, 0, None, None, 10, 128, None, None) == qg.QG_OK
     assert L.quant_table_int8(FAKE, 10, 100, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
     assert L.quant_table_int8(FAKE, 10, 128, MIS, FAKE, None) == qg.QG_ERR_INVALID_ARG
+
+
+def test_rmsnorm_prepare_errors():
+    """Shape, eps, pointer and buffer-size checks of the fused norm+quantiser,
+    all on the host before any launch."""
+    f = qg.lib.rmsnorm_w4a8_prepare
+    need = qg.w4a8_prepared_bytes(4, 256)
+
+    def call(M=4, H=256, ldx=None, eps=1e-6, x=FAKE, w=FAKE, y=FAKE, p=FAKE, pb=need):
+        return f(x, w, M, H, H if ldx is None else ldx, eps, y, p, pb, None)
+
+    assert call(H=200) == qg.QG_ERR_UNSUPPORTED_SHAPE             # H % 128
+    assert call(H=65536 + 128, pb=2 ** 40) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert call(M=-1) == qg.QG_ERR_INVALID_ARG
+    assert call(ldx=128) == qg.QG_ERR_INVALID_ARG
+    assert call(eps=-1e-6) == qg.QG_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == qg.QG_ERR_INVALID_ARG
+    assert call(eps=float("inf")) == qg.QG_ERR_INVALID_ARG
+    assert call(w=None) == qg.QG_ERR_INVALID_ARG
+    assert call(y=MIS) == qg.QG_ERR_INVALID_ARG
+    assert call(pb=need - 1) == qg.QG_ERR_WORKSPACE
+    assert call(M=0, x=None, w=None, y=None, p=None, pb=0) == qg.QG_OK

@@ -201,6 +201,57 @@ def test_w4a8_strided_activations(qg):
 
 
 # ---------------------------------------------------------------------------
+# RMSNorm fused with the quantiser
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,H,pad,eps", [(1, 128, 0, 1e-6), (7, 640, 8, 1e-5), (64, 5120, 0, 1e-6),
+                                         (70, 1280, 0, 0.0), (3, 17408, 0, 1e-6), (2, 65536, 128, 1e-6),
+                                         (16, 2048, 0, 0.5)])
+def test_rmsnorm_prepare_bit_exact(qg, M, H, pad, eps):
+    """y bit-exact against the oracle's norm (every fp32 rounding decides the
+    fp16 outputs and so the codes), and the prepared buffer byte-identical to
+    w4a8_prepare of the oracle's y (whose codes and scales are themselves
+    bit-exact against the oracle quantiser).  Covers one wave through 1024
+    threads x 8 chunks, a strided input, M > 64 (row-major codes), eps = 0
+    with a zero row, a row of outliers and a negative zero.  (Ties of the fp32
+    product between two fp16 values occur a few times per 100k outputs, so
+    the long rows also check the two-step rounding.)"""
+    x = synth.acts(M, H + pad, 1.0, 0.01, 20.0, seed=M * 7 + H)
+    x[0, 3] = -0.0                                    # signed zero keeps its sign through the norm
+    if M > 2:
+        x[1] = 0
+        x[2, ::97] = 3000.0
+    w = (1.0 + 0.25 * synth.acts(1, H, 1.0, 0.0, 1.0, seed=H + 1)[0].astype(np.float32)).astype(np.float16)
+    xd = dev(x)[:, :H]
+    need = qg.w4a8_prepared_bytes(M, H)
+    got = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    y, _ = qg.rmsnorm_w4a8_prepare(xd, dev(w), eps, prepared=got)
+    want_y = oracle.rmsnorm(x[:, :H], w, eps)
+    assert np.array_equal(bits(host(y)), bits(want_y))
+    want = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    qg.w4a8_prepare(dev(want_y), prepared=want)
+    assert torch.equal(got, want)
+    # without the fp16 output the prepared buffer is the same
+    again = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    none, _ = qg.rmsnorm_w4a8_prepare(xd, dev(w), eps, prepared=again, want_y=False)
+    assert none is None and torch.equal(again, want)
+
+
+def test_rmsnorm_prepare_feeds_the_w4a8_gemm(qg):
+    """The fused buffer drives w4a8_gemm_prepared to exactly w4a8_gemm's
+    output on the normalised rows (decode shape)."""
+    cfg = synth.CONFIGS["decode_w4a8"]
+    x, codes, scales = synth.gemm_inputs(cfg)
+    wp, sp = packed(qg, codes, scales)
+    w = (1.0 + 0.25 * synth.acts(1, cfg["K"], 1.0, 0.0, 1.0, seed=77)[0].astype(np.float32)).astype(np.float16)
+    y, prep = qg.rmsnorm_w4a8_prepare(dev(x), dev(w), 1e-6)
+    a = host(qg.w4a8_gemm_prepared(prep, cfg["M"], cfg["K"], wp, sp, cfg["N"]))
+    b = host(qg.w4a8_gemm(y, wp, sp, cfg["N"]))
+    assert np.array_equal(bits(a), bits(b))
+    assert_bounds(a, oracle.ref_w4a8(oracle.rmsnorm(x, w, 1e-6), codes, scales))
+
+
+# ---------------------------------------------------------------------------
 # W4A16
 # ---------------------------------------------------------------------------
 
