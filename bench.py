@@ -18,8 +18,9 @@ the verify (W4A16, M = 8/16, N = 34816), prefill (W4A8, M = 4096, K = 17408)
 and vocabulary (int8 gather + lm_head over 248,320 rows) workloads measured
 the same way, for information, and two lm_head variants: a 40,960-row draft
 head gathered from the int8 table (M = 1) and an int4 head over all 248,320
-rows (W4A16, M = 16 and 64); and the RMSNorm fused with the W4A8 quantiser
-at the decode and prefill shapes.
+rows (W4A16, M = 16 and 64); the RMSNorm fused with the W4A8 quantiser at
+the decode and prefill shapes; and the split-KV verify attention (one layer,
+5 query tokens, 1.5k and 16k context).
 """
 from __future__ import annotations
 
@@ -280,6 +281,28 @@ def extras(torch, qg, synth, np, dev):
         res[f"rmsnorm_w4a8_prepare_m{M}"] = dict(M=M, H=H, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
                                                  frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
         del x, prep, yn
+
+    # split-KV verify attention, one layer: 5 query tokens (1 + 4 drafts), 24
+    # query heads over 4 key/value heads, head_dim 256, 1.5k and 16k context;
+    # caches rotated so that the Infinity Cache cannot serve repeats
+    acfg = synth.CONFIGS["verify_attention"]
+    T, Hq, Hkv = acfg["T"], acfg["Hq"], acfg["Hkv"]
+    for L in acfg["L"]:
+        q, kc, vc = synth.attention_inputs(T, Hq, Hkv, L, acfg["seed"])
+        qd = torch.from_numpy(q).to(dev)
+        kd, vd = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
+        ncopy = copies_for(kd.numel() * 4)
+        caches = [(kd, vd)] + [(kd.clone(), vd.clone()) for _ in range(ncopy - 1)]
+        o = torch.empty((T, Hq, 256), dtype=torch.float16, device=dev)
+        ws = torch.empty((qg.verify_attention_workspace_bytes(T, Hq, Hkv, L),), dtype=torch.uint8, device=dev)
+        us, _ = graph_time_us(torch, lambda i: qg.verify_attention_f16(qd, caches[i % ncopy][0], caches[i % ncopy][1],
+                                                                      o=o, workspace=ws), 2 * ncopy, reps=2)
+        b = 2 * L * Hkv * 256 * 2 + 2 * T * Hq * 256 * 2      # keys and values once, queries and outputs
+        res[f"verify_attention_t{T}_l{L}"] = dict(T=T, Hq=Hq, Hkv=Hkv, L=L, us_per_call=round(us, 3),
+                                                  GBps=round(b / us / 1e3, 1),
+                                                  frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), cache_copies=ncopy)
+        del caches, kd, vd, ws
+        torch.cuda.empty_cache()
 
     cfg = synth.CONFIGS["vocab_int8"]
     V, H = cfg["V"], cfg["H"]

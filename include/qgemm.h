@@ -177,6 +177,28 @@ int rmsnorm_w4a8_prepare(const void* x_f16, const void* w_f16, int64_t M, int64_
                          void* y_f16, void* prepared, size_t prepared_bytes, void* stream);
 
 /*
+ * verify_attention_f16 -- split-KV attention for the speculative-verify step
+ * ([OPT] "In full" item 6: on a multi-query verify step the KV sequence must
+ * be split across workgroups too, or most of the GPU idles; 24 query heads,
+ * head_dim 256 on the pages).  One sequence, T query tokens whose keys and
+ * values are the last T entries of the cache.
+ *   q        fp16 [T][Hq][256], contiguous
+ *   k, v     fp16 [L][Hkv][256], contiguous (the cache, positions 0 .. L-1)
+ *   o        fp16 [T][Hq][256] out:
+ *            o[t][h] = sum_p softmax_p(s) v[p][h/G] over p <= L - T + t, with
+ *            s = (q[t][h] . k[p][h/G]) / 16 and G = Hq / Hkv (grouped-query
+ *            heads); scores, softmax and sums in fp32
+ *   workspace, ws_bytes  >= verify_attention_workspace_bytes(T, Hq, Hkv, L)
+ *            (fp32 per-split partials; no initialisation needed)
+ *   1 <= T <= 16, Hq % Hkv == 0, (Hq / Hkv) * T <= 128, T <= L <= 2^24,
+ *   Hq <= 4096.  Two kernel launches (the splits, then their combination).
+ *   verify_attention_workspace_bytes returns (size_t)-1 for a rejected shape.
+ */
+size_t verify_attention_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t L);
+int verify_attention_f16(const void* q, const void* k_cache, const void* v_cache, int64_t T, int64_t Hq, int64_t Hkv,
+                         int64_t L, void* o, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * w4a8_gemm_debug -- w4a8_gemm that also exposes its integer stages, for
  * bit-exact checks.  Runs the same kernels as w4a8_gemm and in addition
  * writes

@@ -45,7 +45,7 @@ GROUP = 128
 __all__ = [
     "GROUP", "quant_act", "partials", "ref_w4a8", "ref_w4a16", "quant_table",
     "ref_gather", "ref_w8a16", "fp16_bounds", "FP16_MAX_RATIO", "FP16_FROB",
-    "tree_sum_f32", "rmsnorm_factor", "rmsnorm_f32", "rmsnorm", "rmsnorm_quant",
+    "tree_sum_f32", "rmsnorm_factor", "rmsnorm_f32", "rmsnorm", "rmsnorm_quant", "ref_verify_attention",
 ]
 
 # Tolerance for fp16 outputs against the float64 reference:
@@ -141,6 +141,35 @@ def rmsnorm_quant(x, w, eps):
     y = rmsnorm(x, w, eps)
     q, s = quant_act(y)
     return y, q, s
+
+
+def ref_verify_attention(q, k, v):
+    """Causal multi-query attention of the speculative-verify step, float64.
+
+    "In full" item 6 of the optimisations page: the verify step runs attention
+    for several query tokens of one sequence at once (24 query heads,
+    head_dim 256 there).  Reading: the T query tokens are the last T
+    positions of the cache, each sees the cache up to and including its own
+    position, and query heads share key/value heads in groups of
+    G = Hq / Hkv (head h uses key/value head h // G):
+        s[t, h, p] = q[t, h] . k[p, h // G] / sqrt(D),   p <= L - T + t
+        o[t, h]    = sum_p softmax_p(s[t, h, :]) v[p, h // G]
+    q: [T, Hq, D], k and v: [L, Hkv, D] (fp16 values).  Returns float64 [T, Hq, D].
+    """
+    qf = np.asarray(q, dtype=np.float16).astype(np.float64)
+    kf = np.asarray(k, dtype=np.float16).astype(np.float64)
+    vf = np.asarray(v, dtype=np.float16).astype(np.float64)
+    T, Hq, D = qf.shape
+    L, Hkv, _ = kf.shape
+    G = Hq // Hkv
+    visible = np.arange(L)[None, :] <= (L - T + np.arange(T))[:, None]      # [T, L]
+    out = np.empty((T, Hq, D), np.float64)
+    for h in range(Hq):
+        s = qf[:, h, :] @ kf[:, h // G, :].T / np.sqrt(D)                  # [T, L]
+        s = np.where(visible, s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (e / e.sum(axis=1, keepdims=True)) @ vf[:, h // G, :]
+    return out
 
 
 def partials(q, codes):

@@ -8,6 +8,7 @@ library has not been built the import fails; there is no fallback.
 
 Entry points (see ``include/qgemm.h`` for the contract of each):
 act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare, rmsnorm_w4a8_prepare,
+verify_attention_f16,
 w4a8_gemm_prepared, w4a8_gemm_debug,
 w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, plus the size
 helpers w4_packed_bytes, w4_scales_bytes, qg_workspace_bytes and
@@ -53,6 +54,8 @@ _SIGS = {
     "w4a8_prepared_bytes": (_sz, [_i64, _i64]),
     "w4a8_prepare": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _sz, _p]),
     "rmsnorm_w4a8_prepare": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _sz, _p]),
+    "verify_attention_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "verify_attention_f16": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p]),
     "w4a8_gemm_prepared": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "w4a8_gemm_debug": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p,
                                        _p, _p, _p, _i64, _i64, _i64, _i64]),
@@ -199,6 +202,27 @@ def rmsnorm_w4a8_prepare(x, w, eps, prepared=None, y=None, want_y=True):
            lib.rmsnorm_w4a8_prepare(_ptr(x), _ptr(w), M, H, _ldx(x), float(eps), _ptr(y) if want_y else None,
                                     _ptr(prepared), prepared.numel() * prepared.element_size(), _stream(x.device)))
     return (y if want_y else None), prepared
+
+
+def verify_attention_workspace_bytes(T: int, Hq: int, Hkv: int, L: int) -> int:
+    return int(lib.verify_attention_workspace_bytes(T, Hq, Hkv, L))
+
+
+def verify_attention_f16(q, k_cache, v_cache, o=None, workspace=None):
+    """Split-KV attention of q [T, Hq, 256] over the cache k, v [L, Hkv, 256]
+    (the T query tokens are its last T positions, causal among themselves);
+    returns o [T, Hq, 256] fp16."""
+    import torch
+    T, Hq, _ = q.shape
+    L, Hkv, _ = k_cache.shape
+    o = _empty((T, Hq, 256), torch.float16, q) if o is None else o
+    need = verify_attention_workspace_bytes(T, Hq, Hkv, L)
+    if workspace is None:
+        workspace = _empty((max(16, need if need != 2 ** 64 - 1 else 16),), torch.uint8, q)
+    _check("verify_attention_f16",
+           lib.verify_attention_f16(_ptr(q), _ptr(k_cache), _ptr(v_cache), T, Hq, Hkv, L, _ptr(o), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return o
 
 
 def w4a8_gemm_prepared(prepared, M, K, w_packed, s_packed, N, y=None):

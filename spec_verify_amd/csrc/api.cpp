@@ -315,6 +315,38 @@ int rmsnorm_w4a8_prepare(const void* x_f16, const void* w_f16, int64_t M, int64_
                                                 skinny ? q : nullptr, ts, as_stream(stream)));
 }
 
+namespace {
+// Shape rules of verify_attention_f16 (QG_OK or the status to return).
+int check_attention(int64_t T, int64_t Hq, int64_t Hkv, int64_t L) {
+  if (T < 1 || Hq < 1 || Hkv < 1 || L < 1) return QG_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0 || T > 16 || Hq / Hkv * T > 128 || L < T) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (Hq > 4096 || L > (int64_t)1 << 24) return QG_ERR_UNSUPPORTED_SHAPE;
+  return QG_OK;
+}
+}  // namespace
+
+size_t verify_attention_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t L) {
+  if (check_attention(T, Hq, Hkv, L) != QG_OK) return (size_t)-1;
+  return qg::attn_plan(T, Hq, Hkv, L).ws_bytes;
+}
+
+int verify_attention_f16(const void* q, const void* k_cache, const void* v_cache, int64_t T, int64_t Hq, int64_t Hkv,
+                         int64_t L, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_attention(T, Hq, Hkv, L);
+  if (st != QG_OK) return st;
+  if (!q || !k_cache || !v_cache || !o || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(o))
+    return QG_ERR_INVALID_ARG;
+  const qg::AttnPlan pl = qg::attn_plan(T, Hq, Hkv, L);
+  if (!workspace || ws_bytes < pl.ws_bytes) return QG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_verify_attention(
+      reinterpret_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(k_cache),
+      reinterpret_cast<const uint16_t*>(v_cache), reinterpret_cast<uint16_t*>(o), T, Hq, Hkv, L, workspace,
+      as_stream(stream)));
+}
+
 int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, const void* w_packed,
                        const void* s_packed, void* y_f16, void* stream) {
   int st = check_w4a8_shape(M, K, N);

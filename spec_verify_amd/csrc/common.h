@@ -31,6 +31,16 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t M, int64_t H, int64_t ldx, float eps,
                                 uint16_t* y, int8_t* q, int64_t ldq, int8_t* qfrag, float* scale, hipStream_t st);
 
+// Split-KV verify attention (head_dim 256): the split plan and the launch of
+// both passes.  ws holds ws_bytes (fp32 row maxima, sums and partial rows).
+struct AttnPlan {
+  int64_t C, S, R;        // positions per split, splits, query rows per KV head
+  size_t ml_floats, ws_bytes;
+};
+AttnPlan attn_plan(int64_t T, int64_t Hq, int64_t Hkv, int64_t L);
+hipError_t launch_verify_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
+                                   int64_t Hq, int64_t Hkv, int64_t L, void* ws, hipStream_t st);
+
 hipError_t launch_w4_repack(const int8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                             void* w_packed, uint16_t* s_packed, hipStream_t st);
 

@@ -36,7 +36,7 @@ GROUP = 128
 CHUNK_ROWS = 1024
 
 # Stream ids keep the draws for different tensors of one seed independent.
-_S_CODES, _S_SMAG, _S_SSIGN, _S_ACT, _S_OUTL, _S_TABLE, _S_IDS, _S_DRAFT = range(1, 9)
+_S_CODES, _S_SMAG, _S_SSIGN, _S_ACT, _S_OUTL, _S_TABLE, _S_IDS, _S_DRAFT, _S_ATTN = range(1, 10)
 
 _LOG_SMIN = float(np.log(1e-3))
 _LOG_SMAX = float(np.log(1e-2))
@@ -133,6 +133,15 @@ def token_ids(T: int, V: int, seed: int) -> np.ndarray:
     return _rng(seed, _S_IDS, 0).integers(0, V, size=T, dtype=np.int64).astype(np.int32)
 
 
+def attention_inputs(T: int, Hq: int, Hkv: int, L: int, seed: int, D: int = 256):
+    """fp16 queries [T, Hq, D] and key/value caches [L, Hkv, D], all N(0, 1)."""
+    rng = _rng(seed, _S_ATTN, 0)
+    q = rng.standard_normal((T, Hq, D), dtype=np.float32).astype(np.float16)
+    k = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
+    return q, k, v
+
+
 def draft_ids(D: int, V: int, seed: int) -> np.ndarray:
     """A draft vocabulary: D distinct ids of [0, V), ascending, int64.  A
     stand-in of the same size for a list counted over a model's outputs."""
@@ -156,6 +165,10 @@ CONFIGS = {
     "lm_head_w4a16": dict(op="w4a16", M=64, K=5120, N=248320, sigma=1.0, p=0.0, factor=1.0, seed=5),
     "draft_head_int8": dict(op="draft", V=248320, H=5120, D=40960, M=1, sigma=1.0, p=0.0, factor=1.0,
                             table_std=0.02, seed=4),
+    # the verify step's attention, one layer: 1 + 4 draft tokens, 24 query
+    # heads over 4 key/value heads (the key/value head count is a reading),
+    # head_dim 256, the two context lengths the pages measure
+    "verify_attention": dict(op="attention", T=5, Hq=24, Hkv=4, L=(1536, 16384), seed=6),
 }
 
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(qg.lib, n), n
     assert set(names) == set(qg.EXPORTS)
@@ -150,3 +150,24 @@ def test_rmsnorm_prepare_errors():
     assert call(y=MIS) == qg.QG_ERR_INVALID_ARG
     assert call(pb=need - 1) == qg.QG_ERR_WORKSPACE
     assert call(M=0, x=None, w=None, y=None, p=None, pb=0) == qg.QG_OK
+
+
+def test_verify_attention_errors():
+    f = qg.lib.verify_attention_f16
+    need = qg.verify_attention_workspace_bytes(5, 24, 4, 1536)
+    assert 0 < need < 2 ** 40
+
+    def call(T=5, Hq=24, Hkv=4, L=1536, q=FAKE, k=FAKE, v=FAKE, o=FAKE, ws=FAKE, wsb=need):
+        return f(q, k, v, T, Hq, Hkv, L, o, ws, wsb, None)
+
+    assert call(T=0) == qg.QG_ERR_INVALID_ARG
+    assert call(Hkv=5) == qg.QG_ERR_UNSUPPORTED_SHAPE              # Hq % Hkv
+    assert call(T=17) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert call(T=16, Hq=24, Hkv=2) == qg.QG_ERR_UNSUPPORTED_SHAPE  # 12 heads per group x 16 queries > 128 rows
+    assert call(L=4) == qg.QG_ERR_UNSUPPORTED_SHAPE                 # L < T
+    assert call(q=None) == qg.QG_ERR_INVALID_ARG
+    assert call(o=MIS) == qg.QG_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == qg.QG_ERR_WORKSPACE
+    assert call(ws=None) == qg.QG_ERR_WORKSPACE
+    assert call(ws=MIS) == qg.QG_ERR_INVALID_ARG
+    assert qg.verify_attention_workspace_bytes(17, 24, 4, 100) == 2 ** 64 - 1

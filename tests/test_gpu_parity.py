@@ -252,6 +252,44 @@ def test_rmsnorm_prepare_feeds_the_w4a8_gemm(qg):
 
 
 # ---------------------------------------------------------------------------
+# split-KV verify attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,Hq,Hkv,L", [(1, 8, 8, 1), (1, 4, 1, 300), (5, 24, 4, 37), (5, 24, 4, 1536),
+                                        (8, 16, 2, 300), (16, 16, 2, 2000), (16, 24, 4, 16384),
+                                        (3, 6, 3, 8193), (7, 2, 1, 7)])
+def test_verify_attention_within_bounds(qg, T, Hq, Hkv, L):
+    """Against the float64 oracle, element by element, within the fp16 output
+    bounds.  Covers one position, GQA groups of 1 to 8 heads, 16 queries x 8
+    heads (128 rows: two row tiles per wave), a 16k cache (64 splits), a
+    ragged last block and split, and a cache that is only the verify block."""
+    rng = np.random.default_rng(T * 1000 + L)
+    q = rng.standard_normal((T, Hq, 256)).astype(np.float16)
+    k = rng.standard_normal((L, Hkv, 256)).astype(np.float16)
+    v = rng.standard_normal((L, Hkv, 256)).astype(np.float16)
+    o = qg.verify_attention_f16(dev(q), dev(k), dev(v))
+    assert_bounds(host(o).reshape(T, -1), oracle.ref_verify_attention(q, k, v).reshape(T, -1),
+                  f"attention T={T} Hq={Hq} Hkv={Hkv} L={L}")
+
+
+def test_verify_attention_is_causal_and_deterministic(qg):
+    """Changing the cache after query 0's position leaves query 0's output
+    unchanged bit for bit; repeated calls agree bit for bit."""
+    T, Hq, Hkv, L = 5, 24, 4, 700
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((T, Hq, 256)).astype(np.float16)
+    k = rng.standard_normal((L, Hkv, 256)).astype(np.float16)
+    v = rng.standard_normal((L, Hkv, 256)).astype(np.float16)
+    a = host(qg.verify_attention_f16(dev(q), dev(k), dev(v)))
+    b = host(qg.verify_attention_f16(dev(q), dev(k), dev(v)))
+    assert np.array_equal(bits(a), bits(b))
+    k[L - T + 1:] = 9.0
+    v[L - T + 1:] = -4.0
+    c = host(qg.verify_attention_f16(dev(q), dev(k), dev(v)))
+    assert np.array_equal(bits(c[0]), bits(a[0]))
+
+
+# ---------------------------------------------------------------------------
 # W4A16
 # ---------------------------------------------------------------------------
 
