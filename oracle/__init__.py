@@ -19,6 +19,9 @@ stages.  Sources (pages from the open web, cited by title and section):
   group scales are signed (about half negative) and must be honoured.
 * same page, "int8 prefill for single-user mode": prefill runs the same W4A8
   path; decode at batch 64 and speculative verify run W4A16.
+* same page, "In full" item 6: the verify step's sampler takes a small top-k
+  (k <= 64) by selection rather than a sort of the whole 248k-wide row, with
+  a softmax spread over many workgroups.
 * the project README, "What each step buys": the body is W4A16 (int4 weights,
   16-bit activations) and the lm_head/embedding tables are int8.
 
@@ -46,6 +49,7 @@ __all__ = [
     "GROUP", "quant_act", "partials", "ref_w4a8", "ref_w4a16", "quant_table",
     "ref_gather", "ref_w8a16", "fp16_bounds", "FP16_MAX_RATIO", "FP16_FROB",
     "tree_sum_f32", "rmsnorm_factor", "rmsnorm_f32", "rmsnorm", "rmsnorm_quant", "ref_verify_attention",
+    "topk_topp_sample",
 ]
 
 # Tolerance for fp16 outputs against the float64 reference:
@@ -170,6 +174,59 @@ def ref_verify_attention(q, k, v):
         e = np.exp(s - s.max(axis=1, keepdims=True))
         out[:, h, :] = (e / e.sum(axis=1, keepdims=True)) @ vf[:, h // G, :]
     return out
+
+
+def topk_topp_sample(logits, k, top_p, temperature, u):
+    """Small-k top-k / top-p sampling of one step's logits, float64.
+
+    "In full" item 6 of the optimisations page: with k <= 64 known up front,
+    the top-k mask is a plain top-k selection instead of a sort of the whole
+    248k-wide row, the softmax over the row runs on many workgroups, and the
+    target and the drafts sample from the same truncated support.  Readings
+    where the page is silent:
+      * z = x / T with the temperature T given as fp32; the top-k are the k
+        largest logits, larger value first and, among equal values, the
+        lower vocabulary index first (exactly k, ties broken by index);
+      * mass[j] = softmax over those k of z (j = 0 is the largest);
+      * top-p keeps rank j when the mass ranked before it is below p:
+        sum_{i<j} mass[i] < p (so rank 0 is always kept);
+      * probs = mass renormalised over the kept ranks, 0 elsewhere;
+      * the sample is the smallest kept rank j with sum_{i<=j} probs[i] > u
+        for the caller's uniform u in [0, 1) (the last kept rank if none);
+      * lse = log sum_v exp(z_v) over the whole row (the full softmax's
+        normaliser, which needs a finite row maximum).
+    logits fp16 [R, V]; u [R].  Returns a dict of float64/integer arrays:
+    ids [R, k] (int64), mass and probs [R, k], kept [R], sampled [R] (the
+    vocabulary id drawn), rank [R] (its rank) and lse [R].
+    """
+    x = np.asarray(logits, dtype=np.float16)
+    R, V = x.shape
+    xf = x.astype(np.float64)
+    T = float(np.float32(temperature))
+    uf = np.asarray(u, dtype=np.float64).reshape(R)
+    ids = np.empty((R, k), np.int64)
+    mass = np.empty((R, k), np.float64)
+    probs = np.zeros((R, k), np.float64)
+    kept = np.empty(R, np.int64)
+    rank = np.empty(R, np.int64)
+    lse = np.empty(R, np.float64)
+    for r in range(R):
+        order = np.lexsort((np.arange(V), -xf[r]))      # value descending, then index ascending
+        top = order[:k]
+        ids[r] = top
+        z = xf[r, top] / T
+        e = np.exp(z - z[0])
+        mass[r] = e / e.sum()
+        before = np.concatenate(([0.0], np.cumsum(mass[r])[:-1]))
+        kept[r] = int(np.count_nonzero(before < top_p))
+        probs[r, :kept[r]] = mass[r, :kept[r]] / mass[r, :kept[r]].sum()
+        cdf = np.cumsum(probs[r, :kept[r]])
+        rank[r] = min(int(np.count_nonzero(cdf <= uf[r])), kept[r] - 1)
+        zr = xf[r] / T
+        zmax = zr.max()
+        lse[r] = zmax + np.log(np.exp(zr - zmax).sum())
+    sampled = ids[np.arange(R), rank]
+    return dict(ids=ids, mass=mass, probs=probs, kept=kept, rank=rank, sampled=sampled, lse=lse)
 
 
 def partials(q, codes):

@@ -36,7 +36,7 @@ GROUP = 128
 CHUNK_ROWS = 1024
 
 # Stream ids keep the draws for different tensors of one seed independent.
-_S_CODES, _S_SMAG, _S_SSIGN, _S_ACT, _S_OUTL, _S_TABLE, _S_IDS, _S_DRAFT, _S_ATTN = range(1, 10)
+_S_CODES, _S_SMAG, _S_SSIGN, _S_ACT, _S_OUTL, _S_TABLE, _S_IDS, _S_DRAFT, _S_ATTN, _S_LOGIT, _S_UNIF = range(1, 12)
 
 _LOG_SMIN = float(np.log(1e-3))
 _LOG_SMAX = float(np.log(1e-2))
@@ -140,6 +140,30 @@ def attention_inputs(T: int, Hq: int, Hkv: int, L: int, seed: int, D: int = 256)
     k = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
     v = rng.standard_normal((L, Hkv, D), dtype=np.float32).astype(np.float16)
     return q, k, v
+
+
+def sampler_inputs(R: int, V: int, seed: int, sigma: float = 2.0, boosted: int = 8, boost=(6.0, 12.0),
+                   grid: float = 0.0):
+    """fp16 logits [R, V] and uniforms u [R] (float32, in [0, 1)) for the
+    sampler.  Logits are N(0, sigma) with ``boosted`` random ids per row
+    raised by U(boost) (a few likely tokens, as in a language model's
+    output), rounded to fp16; with ``grid`` > 0 they are first rounded to
+    multiples of ``grid``, which makes equal logits common (tie cases)."""
+    x = np.empty((R, V), np.float16)
+
+    def fill(c, r0, r1):
+        rng = _rng(seed, _S_LOGIT, c)
+        v = rng.standard_normal((r1 - r0, V), dtype=np.float32) * np.float32(sigma)
+        for i in range(r1 - r0):
+            hot = rng.choice(V, size=min(boosted, V), replace=False)
+            v[i, hot] += rng.uniform(boost[0], boost[1], size=hot.size).astype(np.float32)
+        if grid > 0:
+            v = np.round(v / np.float32(grid)) * np.float32(grid)
+        x[r0:r1] = v.astype(np.float16)
+
+    _fill_rows(R, fill)
+    u = _rng(seed, _S_UNIF, 0).random(R, dtype=np.float32)
+    return x, u
 
 
 def draft_ids(D: int, V: int, seed: int) -> np.ndarray:
