@@ -199,6 +199,37 @@ int verify_attention_f16(const void* q, const void* k_cache, const void* v_cache
                          int64_t L, void* o, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sample_topk_topp -- small-k top-k / top-p sampling of a step's logits
+ * ([OPT] "In full" item 6: with k <= 64 known up front the mask is a top-k
+ * selection, not a sort of the 248k-wide row; the softmax over the row runs
+ * on many workgroups; target and drafts sample from the same truncated
+ * support).  Per row r of R:
+ *   logits   fp16 [R][ld], the first V values of each row are used
+ *            (ld >= V, ld % 8 == 0, 16-byte aligned); finite or -inf (a
+ *            NaN, or a row that is all -inf, gives undefined results)
+ *   ids      int32 [R][k] out: the k largest logits' ids, larger logit
+ *            first, equal logits by lower id
+ *   probs    fp32 [R][k] out: softmax of logits / T over those k,
+ *            renormalised over the kept ranks, 0 after them
+ *   kept     int32 [R] out: ranks j with sum_{i<j} mass_i < top_p, where
+ *            mass is the softmax over the k (at least 1)
+ *   sampled  int32 [R] out: the id at the smallest kept rank whose
+ *            cumulative probability exceeds u[r] (the last kept rank if
+ *            none); u fp32 [R], the caller's uniforms in [0, 1)
+ *   lse      fp32 [R] out: log sum_v exp(logits[r][v] / T) over all V
+ *   workspace, ws_bytes >= sampler_workspace_bytes(R, V, k) (candidates and
+ *            partial sums; no initialisation needed)
+ *   1 <= k <= 64, k <= V < 2^24, ceil(V / 8192) * k <= 16384, R <= 65536,
+ *   0 < top_p <= 1, 1e-6 <= temperature <= 1e6.  fp32 arithmetic.  Two
+ *   kernel launches (chunks, then rows).  sampler_workspace_bytes returns
+ *   (size_t)-1 for a rejected shape.
+ */
+size_t sampler_workspace_bytes(int64_t R, int64_t V, int64_t k);
+int sample_topk_topp(const void* logits_f16, int64_t R, int64_t V, int64_t ld, int64_t k, float top_p,
+                     float temperature, const float* u, int32_t* ids, float* probs, int32_t* kept, int32_t* sampled,
+                     float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * w4a8_gemm_debug -- w4a8_gemm that also exposes its integer stages, for
  * bit-exact checks.  Runs the same kernels as w4a8_gemm and in addition
  * writes

@@ -8,7 +8,7 @@ library has not been built the import fails; there is no fallback.
 
 Entry points (see ``include/qgemm.h`` for the contract of each):
 act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare, rmsnorm_w4a8_prepare,
-verify_attention_f16,
+verify_attention_f16, sample_topk_topp,
 w4a8_gemm_prepared, w4a8_gemm_debug,
 w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, plus the size
 helpers w4_packed_bytes, w4_scales_bytes, qg_workspace_bytes and
@@ -56,6 +56,9 @@ _SIGS = {
     "rmsnorm_w4a8_prepare": (ctypes.c_int, [_p, _p, _i64, _i64, _i64, ctypes.c_float, _p, _p, _sz, _p]),
     "verify_attention_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "verify_attention_f16": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "sampler_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "sample_topk_topp": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, ctypes.c_float, ctypes.c_float, _p, _p, _p, _p,
+                                        _p, _p, _p, _sz, _p]),
     "w4a8_gemm_prepared": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "w4a8_gemm_debug": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p,
                                        _p, _p, _p, _i64, _i64, _i64, _i64]),
@@ -223,6 +226,32 @@ def verify_attention_f16(q, k_cache, v_cache, o=None, workspace=None):
            lib.verify_attention_f16(_ptr(q), _ptr(k_cache), _ptr(v_cache), T, Hq, Hkv, L, _ptr(o), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(q.device)))
     return o
+
+
+def sampler_workspace_bytes(R: int, V: int, k: int) -> int:
+    return int(lib.sampler_workspace_bytes(R, V, k))
+
+
+def sample_topk_topp(logits, u, k, top_p, temperature, V=None, out=None, workspace=None):
+    """Top-k / top-p sampling of fp16 logits [R, >= V] with uniforms u [R]
+    (fp32).  Returns (ids int32 [R, k], probs fp32 [R, k], kept int32 [R],
+    sampled int32 [R], lse fp32 [R])."""
+    import torch
+    R = logits.shape[0]
+    V = logits.shape[1] if V is None else V
+    if out is None:
+        out = (_empty((R, k), torch.int32, logits), _empty((R, k), torch.float32, logits),
+               _empty((R,), torch.int32, logits), _empty((R,), torch.int32, logits),
+               _empty((R,), torch.float32, logits))
+    ids, probs, kept, sampled, lse = out
+    need = sampler_workspace_bytes(R, V, k)
+    if workspace is None:
+        workspace = _empty((max(16, need if need != 2 ** 64 - 1 else 16),), torch.uint8, logits)
+    _check("sample_topk_topp",
+           lib.sample_topk_topp(_ptr(logits), R, V, _ldx(logits) if R > 0 else V, k, float(top_p), float(temperature),
+                                _ptr(u), _ptr(ids), _ptr(probs), _ptr(kept), _ptr(sampled), _ptr(lse),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(logits.device)))
+    return ids, probs, kept, sampled, lse
 
 
 def w4a8_gemm_prepared(prepared, M, K, w_packed, s_packed, N, y=None):

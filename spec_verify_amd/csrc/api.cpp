@@ -347,6 +347,43 @@ int verify_attention_f16(const void* q, const void* k_cache, const void* v_cache
       as_stream(stream)));
 }
 
+namespace {
+// Shape and parameter rules of sample_topk_topp (QG_OK or the status to return).
+int check_sampler(int64_t R, int64_t V, int64_t k) {
+  if (R < 0 || V < 1 || k < 1) return QG_ERR_INVALID_ARG;
+  if (k > 64 || k > V || R > 65536 || V >= (int64_t)1 << 24) return QG_ERR_UNSUPPORTED_SHAPE;
+  if (qg::sampler_plan(R > 0 ? R : 1, V, k).E == 0) return QG_ERR_UNSUPPORTED_SHAPE;
+  return QG_OK;
+}
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+}  // namespace
+
+size_t sampler_workspace_bytes(int64_t R, int64_t V, int64_t k) {
+  if (check_sampler(R, V, k) != QG_OK) return (size_t)-1;
+  return qg::sampler_plan(R, V, k).ws_bytes;
+}
+
+int sample_topk_topp(const void* logits_f16, int64_t R, int64_t V, int64_t ld, int64_t k, float top_p,
+                     float temperature, const float* u, int32_t* ids, float* probs, int32_t* kept, int32_t* sampled,
+                     float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_sampler(R, V, k);
+  if (st != QG_OK) return st;
+  if (ld < V || ld % 8 != 0) return QG_ERR_INVALID_ARG;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return QG_ERR_INVALID_ARG;
+  if (!(temperature >= 1e-6f && temperature <= 1e6f)) return QG_ERR_INVALID_ARG;
+  if (R == 0) return QG_OK;
+  if (!logits_f16 || !u || !ids || !probs || !kept || !sampled || !lse || !aligned16(logits_f16) || !aligned4(u) ||
+      !aligned4(ids) || !aligned4(probs) || !aligned4(kept) || !aligned4(sampled) || !aligned4(lse))
+    return QG_ERR_INVALID_ARG;
+  const qg::SamplerPlan pl = qg::sampler_plan(R, V, k);
+  if (!workspace || ws_bytes < pl.ws_bytes) return QG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_sampler(reinterpret_cast<const uint16_t*>(logits_f16), R, V, ld, k, top_p,
+                                          temperature, u, ids, probs, kept, sampled, lse, workspace,
+                                          as_stream(stream)));
+}
+
 int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, const void* w_packed,
                        const void* s_packed, void* y_f16, void* stream) {
   int st = check_w4a8_shape(M, K, N);

@@ -41,6 +41,20 @@ AttnPlan attn_plan(int64_t T, int64_t Hq, int64_t Hkv, int64_t L);
 hipError_t launch_verify_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
                                    int64_t Hq, int64_t Hkv, int64_t L, void* ws, hipStream_t st);
 
+// Top-k / top-p sampler: chunks of 256*E logits per pass-1 workgroup, C
+// chunks per row, kpt candidates per pass-2 thread; E == 0 when the shape is
+// beyond the plan (C * k > 16384).
+struct SamplerPlan {
+  int E;
+  int64_t C;
+  int kpt;
+  size_t ws_bytes;
+};
+SamplerPlan sampler_plan(int64_t R, int64_t V, int64_t k);
+hipError_t launch_sampler(const uint16_t* logits, int64_t R, int64_t V, int64_t ld, int64_t k, float top_p,
+                          float temperature, const float* u, int32_t* ids, float* probs, int32_t* kept,
+                          int32_t* sampled, float* lse, void* ws, hipStream_t st);
+
 hipError_t launch_w4_repack(const int8_t* codes, const uint16_t* scales, int64_t N, int64_t K,
                             void* w_packed, uint16_t* s_packed, hipStream_t st);
 

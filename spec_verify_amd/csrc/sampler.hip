@@ -1,0 +1,452 @@
+// Small-k top-k / top-p sampling of one step's logits.
+//
+// Source: "What this repo does that stock vLLM doesn't", "In full" item 6.
+// With top-k <= 64 known up front, the mask needs only the k largest logits
+// of each row, not a sort of the whole 248k-wide row, and the softmax over
+// the row is spread over many workgroups instead of one per row.  Target and
+// drafts sample from the same truncated support.
+//
+// Per row r of fp16 logits x (temperature T, top-k k, top-p p, uniform u):
+//   ids     the k largest logits, larger first, equal values by lower id
+//   mass    softmax of x/T over those k
+//   kept    ranks j with sum_{i<j} mass_i < p (rank 0 always)
+//   probs   mass renormalised over the kept ranks, 0 after them
+//   sampled the id at the smallest kept rank with cumulative probs > u
+//   lse     log sum_v exp(x_v / T) over the whole row
+//
+// Keys.  An element is ranked by the 40-bit key (m(x) << 24) | (2^24-1-id),
+// where m maps fp16 bits to an unsigned code in value order (-inf lowest).
+// Keys are unique, larger key = earlier rank, and key 0 (m = 0 is a NaN
+// pattern, never produced by a real logit) marks padding.
+//
+// Pass 1: one workgroup of 256 threads per (row, chunk of 256*E logits),
+// the chunk held in registers.  The chunk's maximum and sum of
+// exp((x - max)/T) go to the workspace, and so do its k largest keys, found
+// by a radix select (8-bit digits, LDS histogram) over the keys at or above
+// a threshold: the k-th largest of the threads' own maxima.  At least k keys
+// reach that threshold, so the chunk's top k all do, and typically only a
+// few dozen more, which keeps the histogram atomics few.
+// Pass 2: one workgroup of 512 threads per row selects the k largest of the
+// chunks' candidates the same way, sorts them, combines the chunks' partial
+// sums into lse, and one wave forms the softmax over the k, the top-p cut
+// (a wave prefix sum) and the draw.  All in fp32.
+#include "common.h"
+
+namespace qg {
+namespace {
+
+constexpr int kMaxK = 64;
+constexpr int kP1Threads = 256;
+constexpr int kP2Threads = 512;
+constexpr uint32_t kIdMask = 0xFFFFFFu;
+
+__device__ __forceinline__ uint32_t mono16(uint32_t h) { return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u); }
+__device__ __forceinline__ uint32_t unmono16(uint32_t m) { return (m & 0x8000u) ? (m & 0x7FFFu) : (~m & 0xFFFFu); }
+__device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+__device__ __forceinline__ uint64_t key_of(uint32_t m, uint32_t id) {
+  return ((uint64_t)m << 24) | (uint64_t)(kIdMask - id);
+}
+
+struct SelShared {
+  uint32_t hist[256];
+  uint32_t bin, above, hb, cnt;
+  uint64_t list[kMaxK];
+  uint64_t sorted[kMaxK];
+  uint64_t wkey[kP2Threads / 64];
+  float wf[kP2Threads / 64];
+};
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NT>
+__device__ uint64_t block_max_u64(uint64_t v, SelShared& sh) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  if ((threadIdx.x & 63) == 0) sh.wkey[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t r = sh.wkey[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) r = sh.wkey[i] > r ? sh.wkey[i] : r;
+  __syncthreads();
+  return r;
+}
+
+// Sum over the block: wave sums by butterfly, then the waves in order.
+template <int NT>
+__device__ float block_sum_f32(float v, SelShared& sh) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  if ((threadIdx.x & 63) == 0) sh.wf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = sh.wf[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) r += sh.wf[i];
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ float block_max_f32(float v, SelShared& sh) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  if ((threadIdx.x & 63) == 0) sh.wf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = sh.wf[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, sh.wf[i]);
+  __syncthreads();
+  return r;
+}
+
+// Radix select over the block: get(j) is this thread's j-th key when it
+// takes part (0 otherwise).  Returns the largest thr such that at least
+// `need` taking keys are >= thr; when those keys are distinct, exactly
+// `need` of them are.  The caller guarantees at least `need` taking keys.
+// Digits are 8 bits from the top of the 40-bit key; the search stops early
+// once the bucket holding the need-th key is taken whole.
+template <int NT, int KPT, typename Get>
+__device__ uint64_t block_kth(Get get, uint32_t need, SelShared& sh) {
+  uint64_t prefix = 0;
+  int sft = 32;
+  for (int d = 4; d >= 0; --d) {
+    sft = 8 * d;
+    for (int i = threadIdx.x; i < 256; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t q = get(j);
+      if (q != 0 && (q >> (sft + 8)) == prefix) atomicAdd(&sh.hist[(uint32_t)(q >> sft) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // Lane l owns bins 4l .. 4l+3; the keys above them sit in lanes > l.
+      const int l = threadIdx.x;
+      uint32_t hs[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hs[b] = sh.hist[4 * l + b];
+      const uint32_t c = hs[0] + hs[1] + hs[2] + hs[3];
+      uint32_t incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_down((int)incl, o);
+        if (l + o < 64) incl += t;
+      }
+      uint32_t above = incl - c;
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        if (above < need && above + hs[b] >= need) {
+          sh.bin = (uint32_t)(4 * l + b);
+          sh.above = above;
+          sh.hb = hs[b];
+        }
+        above += hs[b];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = sh.bin, above = sh.above, hb = sh.hb;
+    __syncthreads();
+    need -= above;
+    prefix = (prefix << 8) | bin;
+    if (hb == need) break;
+  }
+  return prefix << sft;
+}
+
+// Moves the keys >= thr (distinct, at most kMaxK of them) to sh.list in no
+// particular order; returns how many there are.
+template <int NT, int KPT, typename Get>
+__device__ uint32_t block_collect(Get get, uint64_t thr, SelShared& sh) {
+  if (threadIdx.x == 0) sh.cnt = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint64_t q = get(j);
+    if (q != 0 && q >= thr) {
+      const uint32_t slot = atomicAdd(&sh.cnt, 1u);
+      if (slot < (uint32_t)kMaxK) sh.list[slot] = q;
+    }
+  }
+  __syncthreads();
+  const uint32_t n = sh.cnt;
+  __syncthreads();
+  return n < (uint32_t)kMaxK ? n : (uint32_t)kMaxK;
+}
+
+struct ChunkArgs {
+  const uint16_t* x;
+  int64_t ld;
+  int V, C, k;
+  float c1;              // log2(e) / T
+  uint64_t* wkeys;       // [R][C][k]
+  float2* wstat;         // [R][C]: chunk maximum of x, sum of exp2((x - max) * c1)
+};
+
+template <int E>
+__global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) {
+  constexpr int NT = kP1Threads, NV = E / 8, CH = NT * E;
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int c = (int)(blockIdx.x % (unsigned)a.C);
+  const int r = (int)(blockIdx.x / (unsigned)a.C);
+  const uint16_t* row = a.x + (int64_t)r * a.ld;
+  const int c0 = c * CH;
+  const int nreal = min(CH, a.V - c0);
+
+  // Load: vector i of this thread holds elements c0 + 8 (tid + NT i) + 0..7.
+  uint4 raw[NV];
+  uint32_t mv[E];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int g = c0 + 8 * (tid + NT * i);
+    if (g + 8 <= a.V) {
+      raw[i] = *reinterpret_cast<const uint4*>(row + g);
+    } else {
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (g + t < a.V) w[t >> 1] |= (uint32_t)row[g + t] << (16 * (t & 1));
+      raw[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      mv[8 * i + t] = g + t < a.V ? mono16((w4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu) : 0u;
+  }
+  auto gid = [&](int e) { return (uint32_t)(c0 + 8 * (tid + NT * (e >> 3)) + (e & 7)); };
+
+  // The thread's largest key: elements are visited in id order, so the
+  // first of equal values wins.
+  uint32_t bm = 0;
+  int be = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (mv[e] > bm) { bm = mv[e]; be = e; }
+  const uint64_t tmax = bm ? key_of(bm, gid(be)) : 0;
+
+  // Chunk maximum and sum of exponentials (the full softmax's partials).
+  const uint64_t cmax = block_max_u64<NT>(tmax, sh);
+  const float xmax = h2f(unmono16((uint32_t)(cmax >> 24)));
+  float s = 0.0f;
+  if (xmax != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (mv[8 * i + t] != 0) {
+          const float xv = h2f((w4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
+          s += exp2f((xv - xmax) * a.c1);
+        }
+      }
+    }
+  }
+  s = block_sum_f32<NT>(s, sh);
+
+  // The chunk's k largest keys.
+  const uint32_t k = (uint32_t)a.k;
+  uint64_t thr = 1;                           // every real key
+  if ((uint32_t)nreal > k) {
+    const int nthr = min(NT, (nreal + 7) / 8);   // threads holding a real element
+    uint64_t lo = 1;
+    if ((uint32_t)nthr >= k) {
+      auto getm = [&](int) { return tmax; };
+      lo = block_kth<NT, 1>(getm, k, sh);
+    }
+    const uint32_t lom = (uint32_t)(lo >> 24);
+    auto getk = [&](int e) -> uint64_t {
+      if (mv[e] < lom || mv[e] == 0) return 0;
+      const uint64_t q = key_of(mv[e], gid(e));
+      return q >= lo ? q : 0;
+    };
+    thr = block_kth<NT, E>(getk, k, sh);
+    const uint32_t n = block_collect<NT, E>(getk, thr, sh);
+    (void)n;
+  } else {
+    auto getk = [&](int e) -> uint64_t { return mv[e] ? key_of(mv[e], gid(e)) : 0; };
+    block_collect<NT, E>(getk, thr, sh);
+  }
+  const uint32_t n = min((uint32_t)nreal, k);
+  uint64_t* out = a.wkeys + ((int64_t)r * a.C + c) * a.k;
+  if ((uint32_t)tid < k) out[tid] = (uint32_t)tid < n ? sh.list[tid] : 0;
+  if (tid == 0) a.wstat[(int64_t)r * a.C + c] = make_float2(xmax, s);
+}
+
+struct RowArgs {
+  const uint64_t* wkeys;
+  const float2* wstat;
+  int C, k;
+  float c1, T, top_p;
+  const float* u;
+  int32_t* ids;
+  float* probs;
+  int32_t* kept;
+  int32_t* sampled;
+  float* lse;
+};
+
+template <int KPT>
+__global__ __launch_bounds__(kP2Threads) void sampler_row_kernel(RowArgs a) {
+  constexpr int NT = kP2Threads;
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  const int nk = a.C * a.k;
+  const uint64_t* keys = a.wkeys + (int64_t)r * nk;
+  uint64_t q[KPT];
+  uint64_t tmax = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = tid + NT * j;
+    q[j] = i < nk ? keys[i] : 0;
+    tmax = q[j] > tmax ? q[j] : tmax;
+  }
+  const uint32_t k = (uint32_t)a.k;
+
+  // Threshold from the threads' maxima (when at least k threads hold a
+  // candidate), then the k largest candidates.
+  float cnt = block_sum_f32<NT>(tmax != 0 ? 1.0f : 0.0f, sh);
+  uint64_t lo = 1;
+  if (cnt >= (float)k) {
+    auto getm = [&](int) { return tmax; };
+    lo = block_kth<NT, 1>(getm, k, sh);
+  }
+  auto getk = [&](int j) -> uint64_t { return q[j] >= lo ? q[j] : 0; };
+  const uint64_t thr = block_kth<NT, KPT>(getk, k, sh);
+  block_collect<NT, KPT>(getk, thr, sh);
+
+  // Rank order: the keys are distinct, so ranks are a permutation.
+  if ((uint32_t)tid < k) {
+    const uint64_t mine = sh.list[tid];
+    int rank = 0;
+    for (int i = 0; i < (int)k; ++i) rank += sh.list[i] > mine ? 1 : 0;
+    sh.sorted[rank] = mine;
+  }
+
+  // Full-row log-sum-exp from the chunks' maxima and sums.
+  float xm = -INFINITY;
+  for (int c = tid; c < a.C; c += NT) xm = fmaxf(xm, a.wstat[(int64_t)r * a.C + c].x);
+  const float X = block_max_f32<NT>(xm, sh);
+  float part = 0.0f;
+  for (int c = tid; c < a.C; c += NT) {
+    const float2 st = a.wstat[(int64_t)r * a.C + c];
+    if (st.x != -INFINITY) part += st.y * exp2f((st.x - X) * a.c1);
+  }
+  const float S = block_sum_f32<NT>(part, sh);   // (its barriers also order the sorted[] stores)
+
+  if (tid < 64) {
+    const int j = tid;
+    const bool in = (uint32_t)j < k;
+    const uint64_t key = in ? sh.sorted[j] : 0;
+    const float x = in ? h2f(unmono16((uint32_t)(key >> 24))) : 0.0f;
+    const int id = in ? (int)(kIdMask - (uint32_t)(key & kIdMask)) : 0;
+    const float x0 = __shfl(x, 0);
+    const float e = in ? exp2f((x - x0) * a.c1) : 0.0f;
+    float cum = e;                                   // inclusive prefix sum over the ranks
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(cum, o);
+      if (j >= o) cum += t;
+    }
+    const float total = __shfl(cum, 63);
+    float before = __shfl_up(cum, 1);
+    if (j == 0) before = 0.0f;
+    const uint64_t kb = __ballot(in && before < a.top_p * total);
+    const int nkept = __popcll(kb);                  // a prefix of the ranks; rank 0 always
+    const float ks = __shfl(cum, nkept - 1);
+    const float uu = a.u[r];
+    const uint64_t sb = __ballot(j < nkept && cum <= uu * ks);
+    const int rank = min(__popcll(sb), nkept - 1);
+    const int sid = __shfl(id, rank);
+    if (in) {
+      a.ids[(int64_t)r * a.k + j] = id;
+      a.probs[(int64_t)r * a.k + j] = j < nkept ? e / ks : 0.0f;
+    }
+    if (j == 0) {
+      a.kept[r] = nkept;
+      a.sampled[r] = sid;
+      a.lse[r] = X / a.T + logf(S);
+    }
+  }
+}
+
+int chunk_elems(int64_t R, int64_t V, int64_t k) {
+  // Largest chunk that still gives >= 1024 workgroups, within pass 2's
+  // candidate capacity (C * k <= 512 threads x 32).
+  for (int E : {32, 16, 8}) {
+    const int64_t C = (V + 256 * E - 1) / (256 * E);
+    if (R * C >= 1024 && C * k <= (int64_t)kP2Threads * 32) return E;
+  }
+  for (int E : {8, 16, 32}) {
+    const int64_t C = (V + 256 * E - 1) / (256 * E);
+    if (C * k <= (int64_t)kP2Threads * 32) return E;
+  }
+  return 0;
+}
+
+}  // namespace
+
+SamplerPlan sampler_plan(int64_t R, int64_t V, int64_t k) {
+  SamplerPlan pl{};
+  pl.E = chunk_elems(R, V, k);
+  if (pl.E == 0) return pl;
+  pl.C = (V + 256 * pl.E - 1) / (256 * pl.E);
+  const int64_t per = (pl.C * k + kP2Threads - 1) / kP2Threads;
+  pl.kpt = 1;
+  while (pl.kpt < per) pl.kpt *= 2;
+  pl.ws_bytes = (size_t)(R * pl.C * k) * 8 + (size_t)(R * pl.C) * 8;
+  return pl;
+}
+
+hipError_t launch_sampler(const uint16_t* logits, int64_t R, int64_t V, int64_t ld, int64_t k, float top_p,
+                          float temperature, const float* u, int32_t* ids, float* probs, int32_t* kept,
+                          int32_t* sampled, float* lse, void* ws, hipStream_t st) {
+  const SamplerPlan pl = sampler_plan(R, V, k);
+  ChunkArgs ca;
+  ca.x = logits;
+  ca.ld = ld;
+  ca.V = (int)V;
+  ca.C = (int)pl.C;
+  ca.k = (int)k;
+  ca.c1 = 1.4426950408889634f / temperature;
+  ca.wkeys = reinterpret_cast<uint64_t*>(ws);
+  ca.wstat = reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + (size_t)(R * pl.C * k) * 8);
+  const dim3 g1((unsigned)(R * pl.C));
+  switch (pl.E) {
+    case 32: sampler_chunk_kernel<32><<<g1, kP1Threads, 0, st>>>(ca); break;
+    case 16: sampler_chunk_kernel<16><<<g1, kP1Threads, 0, st>>>(ca); break;
+    default: sampler_chunk_kernel<8><<<g1, kP1Threads, 0, st>>>(ca); break;
+  }
+  RowArgs ra;
+  ra.wkeys = ca.wkeys;
+  ra.wstat = ca.wstat;
+  ra.C = (int)pl.C;
+  ra.k = (int)k;
+  ra.c1 = ca.c1;
+  ra.T = temperature;
+  ra.top_p = top_p;
+  ra.u = u;
+  ra.ids = ids;
+  ra.probs = probs;
+  ra.kept = kept;
+  ra.sampled = sampled;
+  ra.lse = lse;
+  const dim3 g2((unsigned)R);
+  switch (pl.kpt) {
+    case 1: sampler_row_kernel<1><<<g2, kP2Threads, 0, st>>>(ra); break;
+    case 2: sampler_row_kernel<2><<<g2, kP2Threads, 0, st>>>(ra); break;
+    case 4: sampler_row_kernel<4><<<g2, kP2Threads, 0, st>>>(ra); break;
+    case 8: sampler_row_kernel<8><<<g2, kP2Threads, 0, st>>>(ra); break;
+    case 16: sampler_row_kernel<16><<<g2, kP2Threads, 0, st>>>(ra); break;
+    default: sampler_row_kernel<32><<<g2, kP2Threads, 0, st>>>(ra); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qg

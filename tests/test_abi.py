@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(qg.lib, n), n
     assert set(names) == set(qg.EXPORTS)
@@ -171,3 +171,39 @@ def test_verify_attention_errors():
     assert call(ws=None) == qg.QG_ERR_WORKSPACE
     assert call(ws=MIS) == qg.QG_ERR_INVALID_ARG
     assert qg.verify_attention_workspace_bytes(17, 24, 4, 100) == 2 ** 64 - 1
+
+
+def call_sampler(R=2, V=1000, ld=None, k=20, p=0.95, T=1.0, x=FAKE, u=FAKE, out=FAKE, ws=FAKE, wsb=None):
+    wsb = qg.sampler_workspace_bytes(max(R, 1), V, k) if wsb is None else wsb
+    return qg.lib.sample_topk_topp(x, R, V, V if ld is None else ld, k, p, T, u, out, out, out, out, out, ws, wsb,
+                                   None)
+
+
+def test_sampler_sizes():
+    assert qg.sampler_workspace_bytes(64, 248320, 20) > 64 * 20 * 8
+    assert qg.sampler_workspace_bytes(1, 100, 65) == 2 ** 64 - 1         # k > 64
+    assert qg.sampler_workspace_bytes(1, 10, 11) == 2 ** 64 - 1          # k > V
+    assert qg.sampler_workspace_bytes(1, 2 ** 24, 8) == 2 ** 64 - 1      # ids beyond 24 bits
+    assert qg.sampler_workspace_bytes(1, 8192 * 257, 64) == 2 ** 64 - 1  # more candidates than pass 2 holds
+    assert qg.sampler_workspace_bytes(1, 8192 * 256, 64) != 2 ** 64 - 1
+
+
+def test_sampler_argument_errors():
+    assert call_sampler(k=0) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(k=65) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert call_sampler(R=-1) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(p=0.0) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(p=1.5) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(p=float("nan")) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(T=0.0) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(T=float("inf")) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(ld=1004) == qg.QG_ERR_INVALID_ARG                # rows not 16-byte aligned
+    assert call_sampler(ld=992) == qg.QG_ERR_INVALID_ARG                 # ld < V
+    assert call_sampler(x=None) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(x=MIS) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(u=None) == qg.QG_ERR_INVALID_ARG
+    assert call_sampler(ws=None) == qg.QG_ERR_WORKSPACE
+    assert call_sampler(wsb=16) == qg.QG_ERR_WORKSPACE
+    assert call_sampler(ws=MIS) == qg.QG_ERR_INVALID_ARG
+    # no rows: nothing to do, no pointers needed
+    assert call_sampler(R=0, x=None, u=None, out=None, ws=None, wsb=0) == qg.QG_OK
