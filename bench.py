@@ -361,6 +361,29 @@ def extras(torch, qg, synth, np, dev):
                                           TFLOPS=round(2 * M * N * K / us / 1e6, 2), weight_copies=ncopy)
     del wcopies, wp, sp
     torch.cuda.empty_cache()
+
+    # top-k / top-p sampler over the logit rows (copies rotated past the
+    # Infinity Cache); bytes: the logits once, the outputs
+    scfg = synth.CONFIGS["sampler"]
+    V, k = scfg["V"], scfg["k"]
+    for R in scfg["R"]:
+        xs, us_ = synth.sampler_inputs(R, V, scfg["seed"])
+        xs_d = torch.from_numpy(xs).to(dev)
+        ud = torch.from_numpy(us_).to(dev)
+        ncopy = copies_for(xs_d.numel() * 2)
+        lcopies = [xs_d] + [xs_d.clone() for _ in range(ncopy - 1)]
+        outs = (torch.empty((R, k), dtype=torch.int32, device=dev), torch.empty((R, k), dtype=torch.float32, device=dev),
+                torch.empty((R,), dtype=torch.int32, device=dev), torch.empty((R,), dtype=torch.int32, device=dev),
+                torch.empty((R,), dtype=torch.float32, device=dev))
+        ws = torch.empty((qg.sampler_workspace_bytes(R, V, k),), dtype=torch.uint8, device=dev)
+        us, _ = graph_time_us(torch, lambda i: qg.sample_topk_topp(lcopies[i % ncopy], ud, k, scfg["top_p"], scfg["T"],
+                                                                   out=outs, workspace=ws), 2 * ncopy, reps=2)
+        b = R * V * 2 + R * (k * 8 + 12)
+        res[f"sampler_r{R}_v{V}_k{k}"] = dict(R=R, V=V, k=k, top_p=scfg["top_p"], T=scfg["T"], us_per_call=round(us, 3),
+                                             us_per_row=round(us / R, 3), GBps=round(b / us / 1e3, 1),
+                                             frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), logit_copies=ncopy)
+        del lcopies, xs_d, ws
+        torch.cuda.empty_cache()
     return res
 
 

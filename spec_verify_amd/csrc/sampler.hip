@@ -21,15 +21,17 @@
 //
 // Pass 1: one workgroup of 256 threads per (row, chunk of 256*E logits),
 // the chunk held in registers.  The chunk's maximum and sum of
-// exp((x - max)/T) go to the workspace, and so do its k largest keys, found
-// by a radix select (8-bit digits, LDS histogram) over the keys at or above
-// a threshold: the k-th largest of the threads' own maxima.  At least k keys
-// reach that threshold, so the chunk's top k all do, and typically only a
-// few dozen more, which keeps the histogram atomics few.
+// exp((x - max)/T) go to the workspace, and so do its k largest keys in rank
+// order.  Selection: every wave finds the k-th largest of its lanes' own
+// maxima with 40 ballots (at least k keys of the chunk reach it, so all of
+// the chunk's top k do); the keys at or above the largest of those
+// thresholds, typically a few dozen, are compacted to LDS and ranked by
+// counting.  A radix select (8-bit digits, LDS histogram) takes over when
+// more than 512 keys survive.
 // Pass 2: one workgroup of 512 threads per row selects the k largest of the
-// chunks' candidates the same way, sorts them, combines the chunks' partial
-// sums into lse, and one wave forms the softmax over the k, the top-p cut
-// (a wave prefix sum) and the draw.  All in fp32.
+// chunks' candidates the same way, combines the chunks' partial sums into
+// lse, and one wave forms the softmax over the k, the top-p cut (a wave
+// prefix sum) and the draw.  All in fp32.
 #include "common.h"
 
 namespace qg {
@@ -47,10 +49,12 @@ __device__ __forceinline__ uint64_t key_of(uint32_t m, uint32_t id) {
   return ((uint64_t)m << 24) | (uint64_t)(kIdMask - id);
 }
 
+constexpr uint32_t kCap = 512;   // survivors ranked directly; more take the radix select
+
 struct SelShared {
   uint32_t hist[256];
   uint32_t bin, above, hb, cnt;
-  uint64_t list[kMaxK];
+  uint64_t list[kCap];
   uint64_t sorted[kMaxK];
   uint64_t wkey[kP2Threads / 64];
   float wf[kP2Threads / 64];
@@ -179,6 +183,81 @@ __device__ uint32_t block_collect(Get get, uint64_t thr, SelShared& sh) {
   return n < (uint32_t)kMaxK ? n : (uint32_t)kMaxK;
 }
 
+// The k-th largest of the wave's 64 16-bit values (0 when fewer than k are
+// nonzero): the largest t with at least k lanes >= t, built bit by bit with
+// ballots.  No LDS, no barrier.
+__device__ __forceinline__ uint32_t wave_kth16(uint32_t m, uint32_t k) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t tr = t | (1u << b);
+    if ((uint32_t)__popcll(__ballot(m >= tr)) >= k) t = tr;
+  }
+  return t;
+}
+
+// The block's k largest keys, sorted (larger first) into sh.sorted[0..k),
+// zeros after the last when the block holds fewer than k.  get(j, tau)
+// returns this thread's j-th key when it is nonzero and >= tau, else 0;
+// tmaxm is the value code (key >> 24) of this thread's largest key.
+//
+// Threshold: in each wave, the k-th largest of the lanes' value codes is a
+// lower bound of the block's k-th largest value (k keys reach it), and so
+// is the largest of them over the waves; tau is that value with the id bits
+// zero.  The keys >= tau (typically a few dozen) are compacted to LDS, one
+// atomic per wave and step, and ranked by counting; past kCap survivors the
+// radix select takes over.
+template <int NT, int KPT, typename Get>
+__device__ void block_topk(Get get, uint32_t tmaxm, uint32_t k, SelShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t tw = wave_kth16(tmaxm, k);
+  if (lane == 0) sh.wkey[tid >> 6] = tw;
+  if (tid == 0) sh.cnt = 0;
+  for (int i = tid; i < (int)k; i += NT) sh.sorted[i] = 0;
+  __syncthreads();
+  uint64_t tau = sh.wkey[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) tau = sh.wkey[i] > tau ? sh.wkey[i] : tau;
+  tau <<= 24;
+  if (__ballot(tmaxm >= (uint32_t)(tau >> 24) && tmaxm != 0)) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint64_t q = get(j, tau);
+      const uint64_t mask = __ballot(q != 0);
+      if (mask) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sh.cnt, (uint32_t)__popcll(mask));
+        base = (uint32_t)__shfl((int)base, 0);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        if (q != 0 && base + below < kCap) sh.list[base + below] = q;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t n = sh.cnt;
+  __syncthreads();
+  if (n <= kCap) {
+    for (int i = tid; i < (int)n; i += NT) {
+      const uint64_t mine = sh.list[i];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < n; ++j) rank += sh.list[j] > mine ? 1u : 0u;
+      if (rank < k) sh.sorted[rank] = mine;
+    }
+  } else {
+    auto g2 = [&](int j) { return get(j, tau); };
+    const uint64_t thr = block_kth<NT, KPT>(g2, k, sh);
+    block_collect<NT, KPT>(g2, thr, sh);
+    if ((uint32_t)tid < k) {
+      const uint64_t mine = sh.list[tid];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < k; ++j) rank += sh.list[j] > mine ? 1u : 0u;
+      if (rank < k) sh.sorted[rank] = mine;
+    }
+  }
+  __syncthreads();
+}
+
 struct ChunkArgs {
   const uint16_t* x;
   int64_t ld;
@@ -187,6 +266,15 @@ struct ChunkArgs {
   uint64_t* wkeys;       // [R][C][k]
   float2* wstat;         // [R][C]: chunk maximum of x, sum of exp2((x - max) * c1)
 };
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Value codes of two packed fp16 values: h ^ 0x8000 for a positive value,
+// h ^ 0xFFFF for a negative one.
+__device__ __forceinline__ uint32_t mono16x2(uint32_t w) {
+  const uint32_t neg = (w >> 15) & 0x00010001u;
+  return w ^ (0x80008000u | (neg * 0x7FFFu));
+}
 
 template <int E>
 __global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) {
@@ -197,84 +285,69 @@ __global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) 
   const int r = (int)(blockIdx.x / (unsigned)a.C);
   const uint16_t* row = a.x + (int64_t)r * a.ld;
   const int c0 = c * CH;
-  const int nreal = min(CH, a.V - c0);
 
-  // Load: vector i of this thread holds elements c0 + 8 (tid + NT i) + 0..7.
-  uint4 raw[NV];
-  uint32_t mv[E];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int g = c0 + 8 * (tid + NT * i);
-    if (g + 8 <= a.V) {
-      raw[i] = *reinterpret_cast<const uint4*>(row + g);
-    } else {
-      uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (g + t < a.V) w[t >> 1] |= (uint32_t)row[g + t] << (16 * (t & 1));
-      raw[i] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      mv[8 * i + t] = g + t < a.V ? mono16((w4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu) : 0u;
-  }
-  auto gid = [&](int e) { return (uint32_t)(c0 + 8 * (tid + NT * (e >> 3)) + (e & 7)); };
-
-  // The thread's largest key: elements are visited in id order, so the
-  // first of equal values wins.
-  uint32_t bm = 0;
-  int be = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (mv[e] > bm) { bm = mv[e]; be = e; }
-  const uint64_t tmax = bm ? key_of(bm, gid(be)) : 0;
-
-  // Chunk maximum and sum of exponentials (the full softmax's partials).
-  const uint64_t cmax = block_max_u64<NT>(tmax, sh);
-  const float xmax = h2f(unmono16((uint32_t)(cmax >> 24)));
-  float s = 0.0f;
-  if (xmax != -INFINITY) {
+  // Load: vector i of this thread holds elements c0 + 8 (tid + NT i) + 0..7,
+  // as packed fp16 pairs w and their packed value codes mp.  Past V (the
+  // last chunk only) a value reads as -inf, which adds nothing to the sum,
+  // and its code is 0, which is never selected.
+  uint32_t w[E / 2], mp[E / 2];
+  if (c0 + CH <= a.V) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      const uint4 v = *reinterpret_cast<const uint4*>(row + c0 + 8 * (tid + NT * i));
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (mv[8 * i + t] != 0) {
-          const float xv = h2f((w4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
-          s += exp2f((xv - xmax) * a.c1);
-        }
+    for (int i = 0; i < E / 2; ++i) mp[i] = mono16x2(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int g = c0 + 8 * (tid + NT * i);
+      uint32_t h[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) h[t] = g + t < a.V ? (uint32_t)row[g + t] : 0xFC00u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        w[4 * i + t] = h[2 * t] | (h[2 * t + 1] << 16);
+        const uint32_t m = mono16x2(w[4 * i + t]);
+        mp[4 * i + t] = (g + 2 * t < a.V ? m & 0xFFFFu : 0u) | (g + 2 * t + 1 < a.V ? m & 0xFFFF0000u : 0u);
       }
+    }
+  }
+  auto gid = [&](int e) { return (uint32_t)(c0 + 8 * (tid + NT * (e >> 3)) + (e & 7)); };
+  auto code = [&](int e) { return (mp[e >> 1] >> (16 * (e & 1))) & 0xFFFFu; };
+
+  // The thread's largest value code (packed maximum, then the two halves).
+  u16x2 pm = __builtin_bit_cast(u16x2, mp[0]);
+#pragma unroll
+  for (int i = 1; i < E / 2; ++i) pm = __builtin_elementwise_max(pm, __builtin_bit_cast(u16x2, mp[i]));
+  const uint32_t tmaxm = pm.x > pm.y ? pm.x : pm.y;
+
+  // Chunk maximum and sum of exponentials (the full softmax's partials).
+  const uint32_t cmaxm = (uint32_t)block_max_u64<NT>(tmaxm, sh);
+  const float xmax = h2f(unmono16(cmaxm));
+  float s = 0.0f;
+  if (xmax != -INFINITY) {
+    const float off = xmax * a.c1;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      const f16x2 hv = __builtin_bit_cast(f16x2, w[i]);
+      s += __builtin_amdgcn_exp2f(__builtin_fmaf((float)hv.x, a.c1, -off));
+      s += __builtin_amdgcn_exp2f(__builtin_fmaf((float)hv.y, a.c1, -off));
     }
   }
   s = block_sum_f32<NT>(s, sh);
 
-  // The chunk's k largest keys.
+  // The chunk's k largest keys, in rank order.
   const uint32_t k = (uint32_t)a.k;
-  uint64_t thr = 1;                           // every real key
-  if ((uint32_t)nreal > k) {
-    const int nthr = min(NT, (nreal + 7) / 8);   // threads holding a real element
-    uint64_t lo = 1;
-    if ((uint32_t)nthr >= k) {
-      auto getm = [&](int) { return tmax; };
-      lo = block_kth<NT, 1>(getm, k, sh);
-    }
-    const uint32_t lom = (uint32_t)(lo >> 24);
-    auto getk = [&](int e) -> uint64_t {
-      if (mv[e] < lom || mv[e] == 0) return 0;
-      const uint64_t q = key_of(mv[e], gid(e));
-      return q >= lo ? q : 0;
-    };
-    thr = block_kth<NT, E>(getk, k, sh);
-    const uint32_t n = block_collect<NT, E>(getk, thr, sh);
-    (void)n;
-  } else {
-    auto getk = [&](int e) -> uint64_t { return mv[e] ? key_of(mv[e], gid(e)) : 0; };
-    block_collect<NT, E>(getk, thr, sh);
-  }
-  const uint32_t n = min((uint32_t)nreal, k);
+  auto getk = [&](int e, uint64_t tau) -> uint64_t {
+    const uint32_t m = code(e);
+    if (m == 0 || m < (uint32_t)(tau >> 24)) return 0;
+    return key_of(m, gid(e));
+  };
+  block_topk<NT, E>(getk, tmaxm, k, sh);
   uint64_t* out = a.wkeys + ((int64_t)r * a.C + c) * a.k;
-  if ((uint32_t)tid < k) out[tid] = (uint32_t)tid < n ? sh.list[tid] : 0;
+  if ((uint32_t)tid < k) out[tid] = sh.sorted[tid];
   if (tid == 0) a.wstat[(int64_t)r * a.C + c] = make_float2(xmax, s);
 }
 
@@ -299,6 +372,9 @@ __global__ __launch_bounds__(kP2Threads) void sampler_row_kernel(RowArgs a) {
   const int r = blockIdx.x;
   const int nk = a.C * a.k;
   const uint64_t* keys = a.wkeys + (int64_t)r * nk;
+  const float2* stat = a.wstat + (int64_t)r * a.C;
+  // The first NT chunks' partial sums load with the candidates.
+  const float2 st0 = tid < a.C ? stat[tid] : make_float2(-INFINITY, 0.0f);
   uint64_t q[KPT];
   uint64_t tmax = 0;
 #pragma unroll
@@ -309,36 +385,19 @@ __global__ __launch_bounds__(kP2Threads) void sampler_row_kernel(RowArgs a) {
   }
   const uint32_t k = (uint32_t)a.k;
 
-  // Threshold from the threads' maxima (when at least k threads hold a
-  // candidate), then the k largest candidates.
-  float cnt = block_sum_f32<NT>(tmax != 0 ? 1.0f : 0.0f, sh);
-  uint64_t lo = 1;
-  if (cnt >= (float)k) {
-    auto getm = [&](int) { return tmax; };
-    lo = block_kth<NT, 1>(getm, k, sh);
-  }
-  auto getk = [&](int j) -> uint64_t { return q[j] >= lo ? q[j] : 0; };
-  const uint64_t thr = block_kth<NT, KPT>(getk, k, sh);
-  block_collect<NT, KPT>(getk, thr, sh);
-
-  // Rank order: the keys are distinct, so ranks are a permutation.
-  if ((uint32_t)tid < k) {
-    const uint64_t mine = sh.list[tid];
-    int rank = 0;
-    for (int i = 0; i < (int)k; ++i) rank += sh.list[i] > mine ? 1 : 0;
-    sh.sorted[rank] = mine;
-  }
+  auto getk = [&](int j, uint64_t tau) -> uint64_t { return q[j] >= tau ? q[j] : 0; };
+  block_topk<NT, KPT>(getk, (uint32_t)(tmax >> 24), k, sh);
 
   // Full-row log-sum-exp from the chunks' maxima and sums.
-  float xm = -INFINITY;
-  for (int c = tid; c < a.C; c += NT) xm = fmaxf(xm, a.wstat[(int64_t)r * a.C + c].x);
+  float xm = st0.x;
+  for (int c = tid + NT; c < a.C; c += NT) xm = fmaxf(xm, stat[c].x);
   const float X = block_max_f32<NT>(xm, sh);
-  float part = 0.0f;
-  for (int c = tid; c < a.C; c += NT) {
-    const float2 st = a.wstat[(int64_t)r * a.C + c];
+  float part = st0.x != -INFINITY ? st0.y * exp2f((st0.x - X) * a.c1) : 0.0f;
+  for (int c = tid + NT; c < a.C; c += NT) {
+    const float2 st = stat[c];
     if (st.x != -INFINITY) part += st.y * exp2f((st.x - X) * a.c1);
   }
-  const float S = block_sum_f32<NT>(part, sh);   // (its barriers also order the sorted[] stores)
+  const float S = block_sum_f32<NT>(part, sh);
 
   if (tid < 64) {
     const int j = tid;
@@ -377,11 +436,12 @@ __global__ __launch_bounds__(kP2Threads) void sampler_row_kernel(RowArgs a) {
 }
 
 int chunk_elems(int64_t R, int64_t V, int64_t k) {
-  // Largest chunk that still gives >= 1024 workgroups, within pass 2's
-  // candidate capacity (C * k <= 512 threads x 32).
-  for (int E : {32, 16, 8}) {
+  // Enough workgroups to fill the chip several times over (>= 2048) with
+  // chunks of 4096 or 2048 logits, within pass 2's candidate capacity
+  // (C * k <= 512 threads x 32); otherwise the smallest chunk that fits.
+  for (int E : {16, 8}) {
     const int64_t C = (V + 256 * E - 1) / (256 * E);
-    if (R * C >= 1024 && C * k <= (int64_t)kP2Threads * 32) return E;
+    if (R * C >= 2048 && C * k <= (int64_t)kP2Threads * 32) return E;
   }
   for (int E : {8, 16, 32}) {
     const int64_t C = (V + 256 * E - 1) / (256 * E);

@@ -193,6 +193,10 @@ CONFIGS = {
     # heads over 4 key/value heads (the key/value head count is a reading),
     # head_dim 256, the two context lengths the pages measure
     "verify_attention": dict(op="attention", T=5, Hq=24, Hkv=4, L=(1536, 16384), seed=6),
+    # the sampler after the lm_head: 248,320-wide fp16 logit rows, the
+    # model's default sampling (temperature 1.0, top-p 0.95, top-k 20), for
+    # one row, a 1 + 15 verify block and 64 concurrent sequences
+    "sampler": dict(op="sampler", V=248320, R=(1, 16, 64), k=20, top_p=0.95, T=1.0, seed=7),
 }
 
 
