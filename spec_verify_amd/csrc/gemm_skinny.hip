@@ -95,6 +95,8 @@ struct Rsrc {
   __amdgpu_buffer_rsrc_t w, s, x;
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 constexpr uint32_t kOOB = 0x80000000u;   // beyond every resource's extent (checked on the host)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -222,6 +224,78 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
   }
 }
 
+// Epilogue of both weight-streaming kernels: the waves' fp32 sums meet in
+// LDS (red, 2 x NW x QC x 64 f32x4 when the tiles take several chunks) and
+// are added in wave order, then stored as fp16.
+template <int NT, int MT, int NW>
+constexpr int red_chunk() {
+  return NT * MT * NW <= 32 ? NT * MT : 32 / NW;
+}
+template <int NT, int MT, int NW>
+constexpr int red_bufs() {
+  return (NT * MT + red_chunk<NT, MT, NW>() - 1) / red_chunk<NT, MT, NW>() > 1 ? 2 : 1;
+}
+
+template <int MODE, int NT, int MT, int NW>
+__device__ __forceinline__ void sum_and_store(const SkinnyParams& p, const f32x4 (&acc)[NT][MT], int nt0, int nvalid,
+                                              int wave, int lane,
+                                              f32x4 (*red)[NW][red_chunk<NT, MT, NW>()][64]) {
+  // Sum over the waves in wave order, QC (n-tile, m-tile) tiles at a time:
+  // every wave parks its f32x4 per lane and tile in LDS, one barrier, then
+  // thread t of a tile adds the 4 columns 4 (t % 4) .. + 3 of row t / 4 over
+  // the waves and stores them, so consecutive threads write consecutive
+  // bytes of a row.  Value (m, n) of a tile sits in lane m % 16 + 16 (n / 4),
+  // stored at slot lane ^ (lane / 16 % 4) so that the four lanes of a row
+  // fall in distinct LDS banks.  Two buffers alternate (one barrier per
+  // chunk); nothing is stored to global memory before the last barrier.
+  constexpr int Q = NT * MT;                                  // tiles per wave
+  constexpr int QC = Q * NW <= 32 ? Q : 32 / NW;              // tiles per chunk: <= 32 KiB per buffer
+  constexpr int NCH = (Q + QC - 1) / QC;
+  const int tid = (int)threadIdx.x;
+  constexpr int KPC = (QC * 64 + 64 * NW - 1) / (64 * NW);     // sums per thread per chunk
+  f32x4 out[NCH][KPC];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int b = NCH > 1 ? ch & 1 : 0;
+#pragma unroll
+    for (int qq = 0; qq < QC; ++qq) {
+      const int q = ch * QC + qq, j = q / MT, mt = q % MT;
+      if (q < Q) red[b][wave][qq][lane ^ ((lane >> 4) & 3)] = acc[j][mt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KPC; ++k) {
+      const int e = tid + 64 * NW * k;                        // (tile qq, row r, column quad c4)
+      out[ch][k] = (f32x4)0.0f;
+      if (e < QC * 64 && ch * QC + (e >> 6) < Q) {
+        const int qq = e >> 6, r = (e & 63) >> 2, c4 = e & 3;
+        const int l = r + 16 * c4;
+        f32x4 v = red[b][0][qq][l ^ c4];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[b][w][qq][l ^ c4];
+        out[ch][k] = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int k = 0; k < KPC; ++k) {
+      const int e = tid + 64 * NW * k;
+      if (e >= QC * 64 || ch * QC + (e >> 6) >= Q) continue;
+      const int q = ch * QC + (e >> 6), j = q / MT, mt = q % MT, r = (e & 63) >> 2, c4 = e & 3;
+      const int m = mt * 16 + r;
+      if (m >= p.M || j >= nvalid) continue;
+      // W4A8: token scale and the 1/16 of the 16*q weights
+      const float ts = MODE == kW4A8 ? p.tok_scale[m] * 0.0625f : 1.0f;
+      const f32x4 v = out[ch][k];
+      uint2 o;
+      o.x = (uint32_t)float_to_half_bits(v[0] * ts) | ((uint32_t)float_to_half_bits(v[1] * ts) << 16);
+      o.y = (uint32_t)float_to_half_bits(v[2] * ts) | ((uint32_t)float_to_half_bits(v[3] * ts) << 16);
+      *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.N + (nt0 + j) * 16 + 4 * c4) = o;
+    }
+}
+
 template <int MODE, int NT, int MT, int NW, int PF, bool DEBUG>
 __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
   const int lane = threadIdx.x & 63;
@@ -341,62 +415,110 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
     }
   }
 
-  // Sum over the waves in wave order, QC (n-tile, m-tile) tiles at a time:
-  // every wave parks its f32x4 per lane and tile in LDS, one barrier, then
-  // thread t of a tile adds the 4 columns 4 (t % 4) .. + 3 of row t / 4 over
-  // the waves and stores them, so consecutive threads write consecutive
-  // bytes of a row.  Value (m, n) of a tile sits in lane m % 16 + 16 (n / 4),
-  // stored at slot lane ^ (lane / 16 % 4) so that the four lanes of a row
-  // fall in distinct LDS banks.  Two buffers alternate (one barrier per
-  // chunk); nothing is stored to global memory before the last barrier.
-  constexpr int Q = NT * MT;                                  // tiles per wave
-  constexpr int QC = Q * NW <= 32 ? Q : 32 / NW;              // tiles per chunk: <= 32 KiB per buffer
-  constexpr int NCH = (Q + QC - 1) / QC;
-  __shared__ f32x4 red[NCH > 1 ? 2 : 1][NW][QC][64];
-  const int tid = (int)threadIdx.x;
-  constexpr int KPC = (QC * 64 + 64 * NW - 1) / (64 * NW);     // sums per thread per chunk
-  f32x4 out[NCH][KPC];
+  __shared__ f32x4 red[red_bufs<NT, MT, NW>()][NW][red_chunk<NT, MT, NW>()][64];
+  sum_and_store<MODE, NT, MT, NW>(p, acc, nt0, nvalid, wave, lane, red);
+}
+
+// W4A8 at decode size (32 < M <= 64, K <= 5120): everything in flight at
+// once.  In the kernel above each wave's weight loads (HBM latency) and
+// activation loads (L2 hits) share its in-order return queue, and its ring
+// pays the HBM latency once per refill.  Here a workgroup's whole weight and
+// scale slab (2 n-tiles x K/128 groups: at most 80 KiB + 2.5 KiB) moves to
+// LDS with LDS-direct loads, and every wave's activation codes for all of
+// its groups (at most GPW) move to registers, all issued up front; one wait
+// and one barrier later every operand is on the CU.  Groups, their order per
+// wave and the wave sums are those of the kernel above, so the two give
+// bit-identical rows.
+template <int MT, int GPW>
+__global__ __launch_bounds__(512) void decode_w4a8_kernel(SkinnyParams p) {
+  constexpr int NT = 2, NW = 8;
+  constexpr int SLAB = NT * NW * GPW;                 // 1 KiB weight blocks the LDS holds
+  constexpr int SBLK = (SLAB * 32 + 1023) / 1024;     // 1 KiB loads of the slab's scales
+  __shared__ __attribute__((aligned(16))) uint4 wl[SLAB * 64];
+  __shared__ __attribute__((aligned(16))) uint4 sl[SBLK * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, quad = lane >> 4;
+  const int nt0 = blockIdx.x * NT;
+  const int nvalid = min(NT, p.N / 16 - nt0);
+  const uint32_t G = (uint32_t)p.G;
+
+  // The slab is contiguous in both packed layouts: block (tile j, group g)
+  // at (j G + g) KiB, its 16 scales at (j G + g) * 32 B.
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (int64_t)nt0 * G * 1024, (uint32_t)(nvalid * G * 1024));
+  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.s + (int64_t)nt0 * G * 16, (uint32_t)(nvalid * G * 32));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.act, (uint32_t)((int64_t)((p.M + 15) / 16) * 16 * p.K));
+
+  const int ng = wave < p.G ? (p.G - wave + NW - 1) / NW : 0;
+  const int rot = ng > 0 ? (int)(blockIdx.x % (unsigned)ng) : 0;
+  auto gidx = [&](int i) { return wave + NW * (i < ng ? (i + rot < ng ? i + rot : i + rot - ng) : i); };
+
+  // Activation codes of this wave's groups, in fragment order (see
+  // act_quant.hip): one 1 KiB load per (m-tile, half of the group).
+  i32x4 x[GPW][MT][2];
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) {
-    const int b = NCH > 1 ? ch & 1 : 0;
+  for (int i = 0; i < GPW; ++i) {
+    const uint32_t bad = i < ng ? 0u : kOOB;
+    const uint32_t g = (uint32_t)gidx(i);
 #pragma unroll
-    for (int qq = 0; qq < QC; ++qq) {
-      const int q = ch * QC + qq, j = q / MT, mt = q % MT;
-      if (q < Q) red[b][wave][qq][lane ^ ((lane >> 4) & 3)] = acc[j][mt];
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t off = ((((uint32_t)mt * G + g) * 2u) * 64u + lane) * 16u + bad;
+      x[i][mt][0] = __builtin_bit_cast(i32x4, ld128(rx, off));
+      x[i][mt][1] = __builtin_bit_cast(i32x4, ld128(rx, off + 1024u));
     }
-    __syncthreads();
+  }
+  // The slab: wave w fills blocks w, w + NW, ... (past the valid tiles the
+  // loads are out of range and store zeros), then the scales.
 #pragma unroll
-    for (int k = 0; k < KPC; ++k) {
-      const int e = tid + 64 * NW * k;                        // (tile qq, row r, column quad c4)
-      out[ch][k] = (f32x4)0.0f;
-      if (e < QC * 64 && ch * QC + (e >> 6) < Q) {
-        const int qq = e >> 6, r = (e & 63) >> 2, c4 = e & 3;
-        const int l = r + 16 * c4;
-        f32x4 v = red[b][0][qq][l ^ c4];
+  for (int i = 0; i < NT * GPW; ++i) {
+    const int b = wave + NW * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)&wl[b * 64], 16, (uint32_t)(b * 1024 + lane * 16), 0, 0, 0);
+  }
+  if (wave < SBLK)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)&sl[wave * 64], 16, (uint32_t)(wave * 1024 + lane * 16), 0,
+                                             0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x4 acc[NT][MT];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[b][w][qq][l ^ c4];
-        out[ch][k] = v;
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4)0.0f;
+  const uint16_t* sh = reinterpret_cast<const uint16_t*>(sl);
+#pragma unroll
+  for (int i = 0; i < GPW; ++i) {
+    // Stages past the wave's last group multiply zero codes (their
+    // activations were out-of-range loads); their LDS reads stay inside
+    // the slab (group index < NW * GPW).
+    const int g = gidx(i);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int blk = j * (int)G + g;
+      const uint4 wv = blk < SLAB ? wl[blk * 64 + lane] : make_uint4(0, 0, 0, 0);
+      const uint2 sv = blk < SLAB ? *reinterpret_cast<const uint2*>(sh + blk * 16 + 4 * quad) : make_uint2(0, 0);
+      const _Float16 sc[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sv.x & 0xFFFFu)),
+                              __builtin_bit_cast(_Float16, (uint16_t)(sv.x >> 16)),
+                              __builtin_bit_cast(_Float16, (uint16_t)(sv.y & 0xFFFFu)),
+                              __builtin_bit_cast(_Float16, (uint16_t)(sv.y >> 16))};
+      const i32x4 a0 = w4_to_i8x16(wv.x, wv.y);
+      const i32x4 a1 = w4_to_i8x16(wv.z, wv.w);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, x[i][mt][0], (i32x4)0, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, x[i][mt][1], P, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[r], (float)sc[r], acc[j][mt][r]);
       }
     }
   }
-#pragma unroll
-  for (int ch = 0; ch < NCH; ++ch)
-#pragma unroll
-    for (int k = 0; k < KPC; ++k) {
-      const int e = tid + 64 * NW * k;
-      if (e >= QC * 64 || ch * QC + (e >> 6) >= Q) continue;
-      const int q = ch * QC + (e >> 6), j = q / MT, mt = q % MT, r = (e & 63) >> 2, c4 = e & 3;
-      const int m = mt * 16 + r;
-      if (m >= p.M || j >= nvalid) continue;
-      // W4A8: token scale and the 1/16 of the 16*q weights
-      const float ts = MODE == kW4A8 ? p.tok_scale[m] * 0.0625f : 1.0f;
-      const f32x4 v = out[ch][k];
-      uint2 o;
-      o.x = (uint32_t)float_to_half_bits(v[0] * ts) | ((uint32_t)float_to_half_bits(v[1] * ts) << 16);
-      o.y = (uint32_t)float_to_half_bits(v[2] * ts) | ((uint32_t)float_to_half_bits(v[3] * ts) << 16);
-      *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.N + (nt0 + j) * 16 + 4 * c4) = o;
-    }
+  (void)col;
+  __shared__ f32x4 red[red_bufs<NT, MT, NW>()][NW][red_chunk<NT, MT, NW>()][64];
+  sum_and_store<kW4A8, NT, MT, NW>(p, acc, nt0, nvalid, wave, lane, red);
 }
+
+constexpr int kDecodeGPW = 5;   // groups per wave of decode_w4a8_kernel: K <= 8 * 5 * 128
 
 // Prefetch depth: deep enough to keep several 1 KiB weight blocks per wave
 // in flight, shallow enough to leave room for two waves per SIMD.
@@ -463,6 +585,14 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.y = a.y;
   p.dbg = a.dbg;
   p.dm0 = (int)a.dm0; p.dm1 = (int)a.dm1; p.dn0 = (int)a.dn0; p.dn1 = (int)a.dn1;
+  if (a.mode == kW4A8 && a.dbg == nullptr && a.M > 32 && p.G <= 8 * kDecodeGPW && p.N / 16 <= 1024) {
+    const dim3 grid((unsigned)((p.N / 16 + 1) / 2));
+    if (p.M > 48)
+      decode_w4a8_kernel<4, kDecodeGPW><<<grid, dim3(512), 0, st>>>(p);
+    else
+      decode_w4a8_kernel<3, kDecodeGPW><<<grid, dim3(512), 0, st>>>(p);
+    return hipGetLastError();
+  }
   const SkinnyPlan pl = skinny_plan(a.mode, a.N, a.K);
   const dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
   const int mt = (p.M + 15) / 16;
