@@ -142,3 +142,17 @@ def test_same_support_for_target_and_draft_rows(qg):
     assert np.all(ids == ids[0]) and np.all(kept == kept[0]) and np.all(probs == probs[0])
     ranks = [int(np.nonzero(ids[0] == s)[0][0]) for s in sampled]
     assert ranks == sorted(ranks)                    # the draw is monotone in u
+
+
+def test_many_equal_candidates_take_the_radix_select(qg):
+    # A constant row of 300,000 logits at k = 64: every chunk's candidates
+    # tie, so both passes see far more than 512 survivors of the threshold
+    # and select by radix digits; the answer is ids 0 .. 63 in order.
+    V = 300_000
+    x = np.full((2, V), -0.75, np.float16)
+    x[1, ::7] = 0.5                                    # ties among every 7th id
+    u = np.array([0.4, 0.9], np.float32)
+    got = run(qg, x, u, 64, 0.7, 1.0)
+    assert np.array_equal(got[0][0], np.arange(64))
+    assert np.array_equal(got[0][1], np.arange(64) * 7)
+    check(got, oracle.topk_topp_sample(x, 64, 0.7, 1.0, u), u, 0.7)
