@@ -20,16 +20,16 @@
 // pattern, never produced by a real logit) marks padding.
 //
 // Pass 1: one workgroup of 256 threads per (row, chunk of 256*E logits),
-// the chunk held in registers.  The chunk's maximum and sum of
-// exp((x - max)/T) go to the workspace, and so do its k largest keys in rank
-// order.  Selection: every wave finds the k-th largest of its lanes' own
+// the chunk held in registers.  Each wave's maximum and sum of
+// exp((x - max)/T) go to the workspace (shuffles only), and so do the
+// chunk's k largest keys in rank order.  Selection: every wave finds the k-th largest of its lanes' own
 // maxima with 40 ballots (at least k keys of the chunk reach it, so all of
 // the chunk's top k do); the keys at or above the largest of those
 // thresholds, typically a few dozen, are compacted to LDS and ranked by
 // counting.  A radix select (8-bit digits, LDS histogram) takes over when
 // more than 512 keys survive.
 // Pass 2: one workgroup of 512 threads per row selects the k largest of the
-// chunks' candidates the same way, combines the chunks' partial sums into
+// chunks' candidates the same way, combines the waves' partial sums into
 // lse, and one wave forms the softmax over the k, the top-p cut (a wave
 // prefix sum) and the draw.  All in fp32.
 #include "common.h"
@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kMaxK = 64;
 constexpr int kP1Threads = 256;
+constexpr int kWavesP1 = kP1Threads / 64;   // log-sum-exp partials per chunk
 constexpr int kP2Threads = 512;
 constexpr uint32_t kIdMask = 0xFFFFFFu;
 
@@ -59,28 +60,6 @@ struct SelShared {
   uint64_t wkey[kP2Threads / 64];
   float wf[kP2Threads / 64];
 };
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-template <int NT>
-__device__ uint64_t block_max_u64(uint64_t v, SelShared& sh) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  if ((threadIdx.x & 63) == 0) sh.wkey[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint64_t r = sh.wkey[0];
-#pragma unroll
-  for (int i = 1; i < NT / 64; ++i) r = sh.wkey[i] > r ? sh.wkey[i] : r;
-  __syncthreads();
-  return r;
-}
 
 // Sum over the block: wave sums by butterfly, then the waves in order.
 template <int NT>
@@ -236,15 +215,28 @@ __device__ void block_topk(Get get, uint32_t tmaxm, uint32_t k, SelShared& sh) {
   }
   __syncthreads();
   const uint32_t n = sh.cnt;
-  __syncthreads();
   if (n <= kCap) {
+    // Zero keys pad the list to a multiple of 8 (they rank below every
+    // key), so the count below reads 16-byte pairs, four at a time.
+    const uint32_t n8 = (n + 7) & ~7u;
+    if ((uint32_t)tid < n8 - n) sh.list[n + tid] = 0;
+    __syncthreads();
+    const uint4* l2 = reinterpret_cast<const uint4*>(sh.list);
     for (int i = tid; i < (int)n; i += NT) {
       const uint64_t mine = sh.list[i];
       uint32_t rank = 0;
-      for (uint32_t j = 0; j < n; ++j) rank += sh.list[j] > mine ? 1u : 0u;
+      for (uint32_t j = 0; j < n8 / 2; j += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 pr = l2[j + u];
+          rank += (((uint64_t)pr.y << 32) | pr.x) > mine ? 1u : 0u;
+          rank += (((uint64_t)pr.w << 32) | pr.z) > mine ? 1u : 0u;
+        }
+      }
       if (rank < k) sh.sorted[rank] = mine;
     }
   } else {
+    __syncthreads();
     auto g2 = [&](int j) { return get(j, tau); };
     const uint64_t thr = block_kth<NT, KPT>(g2, k, sh);
     block_collect<NT, KPT>(g2, thr, sh);
@@ -264,7 +256,7 @@ struct ChunkArgs {
   int V, C, k;
   float c1;              // log2(e) / T
   uint64_t* wkeys;       // [R][C][k]
-  float2* wstat;         // [R][C]: chunk maximum of x, sum of exp2((x - max) * c1)
+  float2* wstat;         // [R][C][kWavesP1]: each wave's maximum of x, sum of exp2((x - max) * c1)
 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -323,9 +315,13 @@ __global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) 
   for (int i = 1; i < E / 2; ++i) pm = __builtin_elementwise_max(pm, __builtin_bit_cast(u16x2, mp[i]));
   const uint32_t tmaxm = pm.x > pm.y ? pm.x : pm.y;
 
-  // Chunk maximum and sum of exponentials (the full softmax's partials).
-  const uint32_t cmaxm = (uint32_t)block_max_u64<NT>(tmaxm, sh);
-  const float xmax = h2f(unmono16(cmaxm));
+  // The wave's maximum and sum of exponentials (the full softmax's
+  // partials, one pair per wave: shuffles only, no barrier).
+  uint32_t wmaxm = tmaxm;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) wmaxm = max(wmaxm, (uint32_t)__shfl_xor((int)wmaxm, m));
+  // (A wave past the end of the row holds no logit: code 0, maximum -inf.)
+  const float xmax = wmaxm ? h2f(unmono16(wmaxm)) : -INFINITY;
   float s = 0.0f;
   if (xmax != -INFINITY) {
     const float off = xmax * a.c1;
@@ -336,7 +332,9 @@ __global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) 
       s += __builtin_amdgcn_exp2f(__builtin_fmaf((float)hv.y, a.c1, -off));
     }
   }
-  s = block_sum_f32<NT>(s, sh);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if ((tid & 63) == 0) a.wstat[((int64_t)r * a.C + c) * kWavesP1 + (tid >> 6)] = make_float2(xmax, s);
 
   // The chunk's k largest keys, in rank order.
   const uint32_t k = (uint32_t)a.k;
@@ -348,7 +346,6 @@ __global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) 
   block_topk<NT, E>(getk, tmaxm, k, sh);
   uint64_t* out = a.wkeys + ((int64_t)r * a.C + c) * a.k;
   if ((uint32_t)tid < k) out[tid] = sh.sorted[tid];
-  if (tid == 0) a.wstat[(int64_t)r * a.C + c] = make_float2(xmax, s);
 }
 
 struct RowArgs {
@@ -372,9 +369,10 @@ __global__ __launch_bounds__(kP2Threads) void sampler_row_kernel(RowArgs a) {
   const int r = blockIdx.x;
   const int nk = a.C * a.k;
   const uint64_t* keys = a.wkeys + (int64_t)r * nk;
-  const float2* stat = a.wstat + (int64_t)r * a.C;
-  // The first NT chunks' partial sums load with the candidates.
-  const float2 st0 = tid < a.C ? stat[tid] : make_float2(-INFINITY, 0.0f);
+  const int nst = a.C * kWavesP1;
+  const float2* stat = a.wstat + (int64_t)r * nst;
+  // The first NT of the chunks' partial sums load with the candidates.
+  const float2 st0 = tid < nst ? stat[tid] : make_float2(-INFINITY, 0.0f);
   uint64_t q[KPT];
   uint64_t tmax = 0;
 #pragma unroll
@@ -390,10 +388,10 @@ __global__ __launch_bounds__(kP2Threads) void sampler_row_kernel(RowArgs a) {
 
   // Full-row log-sum-exp from the chunks' maxima and sums.
   float xm = st0.x;
-  for (int c = tid + NT; c < a.C; c += NT) xm = fmaxf(xm, stat[c].x);
+  for (int c = tid + NT; c < nst; c += NT) xm = fmaxf(xm, stat[c].x);
   const float X = block_max_f32<NT>(xm, sh);
   float part = st0.x != -INFINITY ? st0.y * exp2f((st0.x - X) * a.c1) : 0.0f;
-  for (int c = tid + NT; c < a.C; c += NT) {
+  for (int c = tid + NT; c < nst; c += NT) {
     const float2 st = stat[c];
     if (st.x != -INFINITY) part += st.y * exp2f((st.x - X) * a.c1);
   }
@@ -460,7 +458,7 @@ SamplerPlan sampler_plan(int64_t R, int64_t V, int64_t k) {
   const int64_t per = (pl.C * k + kP2Threads - 1) / kP2Threads;
   pl.kpt = 1;
   while (pl.kpt < per) pl.kpt *= 2;
-  pl.ws_bytes = (size_t)(R * pl.C * k) * 8 + (size_t)(R * pl.C) * 8;
+  pl.ws_bytes = (size_t)(R * pl.C * k) * 8 + (size_t)(R * pl.C * kWavesP1) * 8;
   return pl;
 }
 
