@@ -54,6 +54,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Packed int4 weights are read once per call, in full lines: non-temporal
+// hint (aux bit 1).  The int8 table rows keep the default policy (the two
+// halves of a line arrive in two loads).
+__device__ __forceinline__ uint4 ld128_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 
 // LDS-direct loads: lane l's bytes from r + voff + soff land at lds + 16 l
 // (16-byte loads) or lds + 4 l (4- and 2-byte loads; a 2-byte value is
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void wide_kernel(WideParams p) {
     for (int j = 0; j < TPW; ++j) {
       const uint32_t tj = (uint32_t)(wt0 + j);
       if constexpr (MODE == kW4A16) {
-        st.w[j] = ld128(rsw, ((tj * (uint32_t)G + (uint32_t)g) * 64u + lane) * 16u | bad);
+        st.w[j] = ld128_stream(rsw, ((tj * (uint32_t)G + (uint32_t)g) * 64u + lane) * 16u | bad);
       } else {
         const uint32_t row = (tj * 16u + col) * (uint32_t)p.K + (uint32_t)g * 128u + 16u * quad;
         st.w[j][0] = ld128(rsw, row | bad);
