@@ -286,7 +286,9 @@ __global__ __launch_bounds__(kP1Threads) void sampler_chunk_kernel(ChunkArgs a) 
   if (c0 + CH <= a.V) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const uint4 v = *reinterpret_cast<const uint4*>(row + c0 + 8 * (tid + NT * i));
+      // logits are read once: non-temporal hint
+      const uint4 v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(row + c0 + 8 * (tid + NT * i))));
       w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
 #pragma unroll
