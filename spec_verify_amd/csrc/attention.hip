@@ -238,10 +238,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
 AttnPlan attn_plan(int64_t T, int64_t Hq, int64_t Hkv, int64_t L) {
   AttnPlan pl;
   const int64_t G = Hq / Hkv, R = T * G;
-  // about 256 workgroups in pass 1, but at least 4 blocks (128 positions)
-  // per split, so that the per-split partial rows stay small next to the
-  // cache they summarise; splits are a multiple of 32 positions
-  int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + Hkv - 1) / Hkv, (L + 4 * kBlk - 1) / (4 * kBlk)));
+  // About 256 workgroups in pass 1 (splits are a multiple of 32 positions,
+  // at least one block).  Short caches get as many splits as they have
+  // blocks: at 1.5k positions, 48 splits of one block ran in 14.6 us, 12
+  // splits of four in 20.9 us (the per-split partial rows then outweigh the
+  // cache, but pass 1 fills the GPU).  More than 256 workgroups made long
+  // caches slower (16k positions: 44 us at 512 against 38 us), as pass 2
+  // has more partial rows to read.
+  int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + Hkv - 1) / Hkv, (L + kBlk - 1) / kBlk));
   int64_t C = ((L + S - 1) / S + kBlk - 1) / kBlk * kBlk;
   S = (L + C - 1) / C;
   pl.C = C;
