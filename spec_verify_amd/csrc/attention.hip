@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
 
 // Pass 2: one workgroup of 256 threads (one per dimension) per (KV head, row).
 // The splits' maxima and sums go to LDS first; each thread then reads its
-// dimension of every split's row, 8 loads in flight at a time.
+// dimension of every split's row, 16 loads in flight at a time.
 constexpr int kMaxSplits = 256;   // attn_plan never makes more
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int kvh = blockIdx.y, row = blockIdx.x, dim = threadIdx.x;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   float M = -__builtin_inff();
   for (int s = 0; s < p.S; ++s) M = fmaxf(M, ml[2 * s]);
   float num = 0.0f, den = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
   for (int s = 0; s < p.S; ++s) {
     const float ms = ml[2 * s];
     const float w = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
