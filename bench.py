@@ -220,7 +220,7 @@ def main():
         max(ncopy, 200))
     kernel_bytes = N * K // 2 + N * (K // 128) * 2 + M * K + M * 4 + M * N * 2
     achieved = kernel_bytes / (gemm_us * 1e-6) / 1e9
-    roofline = dict(bound="hbm", kernel="decode_w4a8_kernel<4, 5> (w4a8_gemm_prepared)", achieved=round(achieved, 1),
+    roofline = dict(bound="hbm", kernel="skinny_kernel<W4A8, 5 n-tiles, 1 m-tile, 8 waves, ring 1> (rows split over 4 workgroups, w4a8_gemm_prepared)", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                     bytes_per_launch=kernel_bytes, avg_launch_us=round(gemm_us, 3), traffic=measured_traffic())
 

@@ -447,14 +447,24 @@ def test_empty_batch_is_a_no_op(qg):
 
 @pytest.mark.parametrize("op", ["w4a8", "w4a16"])
 def test_rows_do_not_depend_on_the_batch(qg, op):
-    """A token's output does not change with the other tokens in the batch
-    (M = 1, 8, 16, 64 all take the weight-streaming kernel): bit-identical."""
+    """A token's output does not change with the other tokens in the batch,
+    bit for bit, within each kernel regime: W4A16 takes the weight-streaming
+    kernel at M = 1 .. 64 here; W4A8 takes it at M <= 16 and its row-split
+    form at 16 < M <= 64 (one 16-row m-tile per workgroup, the same group
+    order for every m-tile), which adds the groups in another order than
+    the M <= 16 form."""
     cfg = synth.CONFIGS["decode_w4a8"]
     x, codes, scales = synth.gemm_inputs(cfg)
     wp, sp = packed(qg, codes, scales)
     fn = qg.w4a8_gemm if op == "w4a8" else qg.w4a16_gemm
     full = host(fn(dev(x), wp, sp, cfg["N"]))
-    for M in (1, 8, 16):
+    small = host(fn(dev(x[:16]), wp, sp, cfg["N"]))
+    for M in (1, 8):
+        part = host(fn(dev(x[:M]), wp, sp, cfg["N"]))
+        assert np.array_equal(bits(part), bits(small[:M])), M
+    if op == "w4a16":
+        assert np.array_equal(bits(small), bits(full[:16]))
+    for M in (17, 33, 48):
         part = host(fn(dev(x[:M]), wp, sp, cfg["N"]))
         assert np.array_equal(bits(part), bits(full[:M])), M
 
