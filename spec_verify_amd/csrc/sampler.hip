@@ -43,7 +43,6 @@ constexpr int kWavesP1 = kP1Threads / 64;   // log-sum-exp partials per chunk
 constexpr int kP2Threads = 512;
 constexpr uint32_t kIdMask = 0xFFFFFFu;
 
-__device__ __forceinline__ uint32_t mono16(uint32_t h) { return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u); }
 __device__ __forceinline__ uint32_t unmono16(uint32_t m) { return (m & 0x8000u) ? (m & 0x7FFFu) : (~m & 0xFFFFu); }
 __device__ __forceinline__ float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 __device__ __forceinline__ uint64_t key_of(uint32_t m, uint32_t id) {
