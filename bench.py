@@ -134,6 +134,36 @@ def graph_time_us(torch, fn, n_calls, reps=1):
     return e0.elapsed_time(e1) * 1e3 / (n_calls * reps), g
 
 
+def clocks_under_load(torch, graph, replays):
+    """Clocks and socket power read with amd-smi while `graph` replays
+    (`replays` times, enqueued before the query so the GPU is busy while it
+    runs).  None when amd-smi is missing or fails; the bench never depends
+    on it."""
+    import shutil
+    import subprocess
+    smi = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if smi is None:
+        return None
+    for _ in range(replays):
+        graph.replay()
+    try:
+        r = subprocess.run([smi, "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        torch.cuda.synchronize()
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = g["clock"]
+        gfx = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem_") and isinstance(v.get("clk"), dict)]
+        gmax = [v["max_clk"]["value"] for k, v in clk.items() if k.startswith("gfx_") and isinstance(v.get("max_clk"), dict)]
+        pw = g.get("power", {}).get("socket_power", {})
+        return dict(source="amd-smi metric -c -p during graph replay", gfx_mhz=gfx, gfx_max_mhz=max(gmax) if gmax else None,
+                    mem_mhz=mem, socket_power_w=pw.get("value") if isinstance(pw, dict) else None)
+    except Exception:  # noqa: BLE001 -- reporting only
+        torch.cuda.synchronize()
+        return None
+
+
 def cpu_baseline(x, codes, scales, seconds):
     """The numpy oracle (quantise, exact group partials, float64 rescale) on the
     decode workload, repeated for about `seconds` on the host's cores."""
@@ -233,6 +263,9 @@ def main():
                            M=M, K=K, N=N, weight_copies=ncopy, graph_replay=True),
                tops=round(2 * M * N * K / (ms_per_step * 1e-3) / 1e12, 3),
                frac_hbm=round(value / HBM_PEAK_GBS, 4), wall_s=round(wall, 4), roofline=roofline)
+
+    # SCLK / MCLK and socket power while the timed graph replays (about a second)
+    out["clocks"] = clocks_under_load(torch, g, max(1, int(1.0 / max(ms * 1e-3, 1e-6))))
 
     if not args.no_extra:
         out["per_workload"] = extras(torch, qg, synth, np, dev)
