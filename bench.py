@@ -264,8 +264,10 @@ def main():
                tops=round(2 * M * N * K / (ms_per_step * 1e-3) / 1e12, 3),
                frac_hbm=round(value / HBM_PEAK_GBS, 4), wall_s=round(wall, 4), roofline=roofline)
 
-    # SCLK / MCLK and socket power while the timed graph replays (about a second)
-    out["clocks"] = clocks_under_load(torch, g, max(1, int(1.0 / max(ms * 1e-3, 1e-6))))
+    # SCLK / MCLK and socket power while the timed graph replays (about three
+    # seconds of replays are queued, so the GPU is still busy when amd-smi,
+    # which takes a second or more to start, reads them)
+    out["clocks"] = clocks_under_load(torch, g, max(1, int(3.0 / max(ms * 1e-3, 1e-6))))
 
     if not args.no_extra:
         out["per_workload"] = extras(torch, qg, synth, np, dev)
