@@ -44,6 +44,8 @@ struct SkinnyParams {
   const uint16_t* s;
   int M, N, K, G;
   int ms;                   // m-groups: workgroups that share an n-block, each with MT m-tiles
+  int wgs;                  // n-blocks of unequal size (0: NT tiles each): block b has tiles
+                            // [b T / wgs, (b + 1) T / wgs) of the T n-tiles
   uint16_t* y;
   int32_t* dbg;
   int dm0, dm1, dn0, dn1;
@@ -325,9 +327,9 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
     nb = (int)(lin / (unsigned)p.ms);
     mg = (int)(lin % (unsigned)p.ms);
   }
-  const int nt0 = nb * NT;
+  const int nt0 = p.wgs ? (int)((int64_t)nb * (p.N / 16) / p.wgs) : nb * NT;
   const int mt0 = mg * MT;
-  const int nvalid = min(NT, p.N / 16 - nt0);
+  const int nvalid = p.wgs ? (int)((int64_t)(nb + 1) * (p.N / 16) / p.wgs) - nt0 : min(NT, p.N / 16 - nt0);
 
   f32x4 acc[NT][MT];
 #pragma unroll
@@ -552,6 +554,7 @@ constexpr int kDecodeGPW = 5;   // groups per wave of decode_w4a8_kernel: K <= 8
 // W4A8 at 16 < M <= 64 when N / 16 is a multiple of 5: the streaming
 // kernel with the rows split over workgroups (see launch_skinny).
 constexpr int kMsplitNT = 5, kMsplitPF = 1;
+constexpr int kBalancedWgs = 512;   // two workgroups per CU
 
 // Prefetch depth: deep enough to keep several 1 KiB weight blocks per wave
 // in flight, shallow enough to leave room for two waves per SIMD.
@@ -619,6 +622,7 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.dbg = a.dbg;
   p.dm0 = (int)a.dm0; p.dm1 = (int)a.dm1; p.dn0 = (int)a.dn0; p.dn1 = (int)a.dn1;
   p.ms = 1;
+  p.wgs = 0;
   // W4A8 at 16 < M <= 64 (decode batches): one 16-row m-tile and 5 n-tiles
   // per workgroup, 8 waves splitting K, a one-stage ring.  Each CU then
   // pulls 82 KB of activation codes and 200 KB of weights (most of them L2
@@ -642,8 +646,21 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const SkinnyPlan pl = skinny_plan(a.mode, a.N, a.K);
-  const dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
   const int mt = (p.M + 15) / 16;
+  // fp16-activation products over 1024 .. 2560 n-tiles (the verify
+  // projections, the draft head): blocks of four n-tiles leave some CUs
+  // with one workgroup more than the rest (544 workgroups for N = 34,816),
+  // and those set the time; 512 blocks of four or five tiles give every CU
+  // two.
+  if (a.mode != kW4A8 && a.dbg == nullptr && pl.nt == 4 && p.N / 16 > 1024 && p.N / 16 <= 5 * kBalancedWgs) {
+    p.wgs = kBalancedWgs;
+    if (a.mode == kW4A16)
+      launch_mt<kW4A16, 5, 4, false>(p, mt, dim3((unsigned)kBalancedWgs), st);
+    else
+      launch_mt<kW8A16, 5, 4, false>(p, mt, dim3((unsigned)kBalancedWgs), st);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
   switch (a.mode) {
     case kW4A8:
       return a.dbg ? launch_mode<kW4A8, true>(p, pl, mt, grid, st) : launch_mode<kW4A8, false>(p, pl, mt, grid, st);
