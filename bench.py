@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-workload extras")
+    ap.add_argument("--extras", default=",".join(EXTRA_SECTIONS),
+                    help="comma list of the per-workload sections to run: " + ", ".join(EXTRA_SECTIONS))
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the amd-smi clock reading (also skipped under rocprofv3, whose preloaded "
+                         "library would follow amd-smi into its child process)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates the FETCH_SIZE / WRITE_SIZE "
@@ -267,18 +272,27 @@ def main():
     # SCLK / MCLK and socket power while the timed graph replays (about three
     # seconds of replays are queued, so the GPU is still busy when amd-smi,
     # which takes a second or more to start, reads them)
-    out["clocks"] = clocks_under_load(torch, g, max(1, int(3.0 / max(ms * 1e-3, 1e-6))))
+    under_profiler = any(k.startswith("ROCPROF") for k in os.environ)
+    out["clocks"] = (None if args.no_clocks or under_profiler
+                     else clocks_under_load(torch, g, max(1, int(3.0 / max(ms * 1e-3, 1e-6)))))
 
     if not args.no_extra:
-        out["per_workload"] = extras(torch, qg, synth, np, dev)
+        out["per_workload"] = extras(torch, qg, synth, np, dev, set(args.extras.split(",")))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, codes, scales, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def extras(torch, qg, synth, np, dev):
+EXTRA_SECTIONS = ("gemm", "norm", "attention", "vocab", "heads", "sampler")
+
+
+def extras(torch, qg, synth, np, dev, sections):
     res = {}
-    for name in ("verify_w4a16_m8", "verify_w4a16_m16", "prefill_w4a8"):
+
+    def done(section):
+        print(f"# bench: {section} measured", file=sys.stderr, flush=True)
+
+    for name in (("verify_w4a16_m8", "verify_w4a16_m16", "prefill_w4a8") if "gemm" in sections else ()):
         cfg = synth.CONFIGS[name]
         M, K, N = cfg["M"], cfg["K"], cfg["N"]
         x, codes, scales = synth.gemm_inputs(cfg)
@@ -301,10 +315,11 @@ def extras(torch, qg, synth, np, dev):
                          frac_mfma=round(ops / us / 1e6 / peak_ops, 4), weight_copies=ncopy)
         del copies, wp, sp
         torch.cuda.empty_cache()
+        done(name)
 
     # the quantiser fused into the norm that makes its input (one launch per
     # hidden state; the prepared buffer then feeds every W4A8 GEMM of it)
-    for name in ("decode_w4a8", "prefill_w4a8"):
+    for name in (("decode_w4a8", "prefill_w4a8") if "norm" in sections else ()):
         cfg = synth.CONFIGS[name]
         M, H = cfg["M"], cfg["K"]
         x = torch.from_numpy(synth.acts(M, H, cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)).to(dev)
@@ -316,13 +331,14 @@ def extras(torch, qg, synth, np, dev):
         res[f"rmsnorm_w4a8_prepare_m{M}"] = dict(M=M, H=H, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
                                                  frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4))
         del x, prep, yn
+        done(f"rmsnorm_w4a8_prepare_m{M}")
 
     # split-KV verify attention, one layer: 5 query tokens (1 + 4 drafts), 24
     # query heads over 4 key/value heads, head_dim 256, 1.5k and 16k context;
     # caches rotated so that the Infinity Cache cannot serve repeats
     acfg = synth.CONFIGS["verify_attention"]
     T, Hq, Hkv = acfg["T"], acfg["Hq"], acfg["Hkv"]
-    for L in acfg["L"]:
+    for L in (acfg["L"] if "attention" in sections else ()):
         q, kc, vc = synth.attention_inputs(T, Hq, Hkv, L, acfg["seed"])
         qd = torch.from_numpy(q).to(dev)
         kd, vd = torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev)
@@ -338,24 +354,43 @@ def extras(torch, qg, synth, np, dev):
                                                   frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), cache_copies=ncopy)
         del caches, kd, vd, ws
         torch.cuda.empty_cache()
+        done(f"verify_attention_t{T}_l{L}")
+    if not sections & {"vocab", "heads", "sampler"}:
+        return res
 
     cfg = synth.CONFIGS["vocab_int8"]
     V, H = cfg["V"], cfg["H"]
-    src = torch.from_numpy(synth.table_source(V, H, cfg["seed"] + 200).view(np.int16)).to(dev)
-    Q, S = qg.quant_table_int8(src)
-    del src
-    ids = torch.from_numpy(synth.token_ids(cfg["T"], V, cfg["seed"] + 300)).to(dev)
-    out = torch.empty((cfg["T"], H), dtype=torch.float16, device=dev)
-    us, _ = graph_time_us(torch, lambda i: qg.embed_gather_dequant_int8(ids, Q, S, out=out), 200)
-    res["vocab_gather_t64"] = dict(T=cfg["T"], H=H, us_per_call=round(us, 3),
-                                   bytes=cfg["T"] * (H + H // 128 * 2 + H * 2))
-    x = torch.from_numpy(synth.acts(cfg["M"], H, cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)).to(dev)
-    y = torch.empty((cfg["M"], V), dtype=torch.float16, device=dev)
-    us, _ = graph_time_us(torch, lambda i: qg.w8a16_gemm(x, Q, S, y=y), 10, reps=2)
-    b = V * H + V * (H // 128) * 2 + cfg["M"] * H * 2 + cfg["M"] * V * 2
-    res["lm_head_w8a16_m64"] = dict(M=cfg["M"], K=H, N=V, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
-                                    frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                                    TFLOPS=round(2 * cfg["M"] * V * H / us / 1e6, 2))
+    if sections & {"vocab", "heads"}:
+        src = torch.from_numpy(synth.table_source(V, H, cfg["seed"] + 200).view(np.int16)).to(dev)
+        Q, S = qg.quant_table_int8(src)
+        del src
+    if "vocab" in sections:
+        ids = torch.from_numpy(synth.token_ids(cfg["T"], V, cfg["seed"] + 300)).to(dev)
+        out = torch.empty((cfg["T"], H), dtype=torch.float16, device=dev)
+        us, _ = graph_time_us(torch, lambda i: qg.embed_gather_dequant_int8(ids, Q, S, out=out), 200)
+        res["vocab_gather_t64"] = dict(T=cfg["T"], H=H, us_per_call=round(us, 3),
+                                       bytes=cfg["T"] * (H + H // 128 * 2 + H * 2))
+        x = torch.from_numpy(synth.acts(cfg["M"], H, cfg["sigma"], cfg["p"], cfg["factor"], cfg["seed"] + 100)).to(dev)
+        y = torch.empty((cfg["M"], V), dtype=torch.float16, device=dev)
+        us, _ = graph_time_us(torch, lambda i: qg.w8a16_gemm(x, Q, S, y=y), 10, reps=2)
+        b = V * H + V * (H // 128) * 2 + cfg["M"] * H * 2 + cfg["M"] * V * 2
+        res["lm_head_w8a16_m64"] = dict(M=cfg["M"], K=H, N=V, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
+                                        frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                                        TFLOPS=round(2 * cfg["M"] * V * H / us / 1e6, 2))
+        del y
+        done("vocab_gather_t64, lm_head_w8a16_m64")
+    if "heads" in sections:
+        res.update(head_variants(torch, qg, synth, dev, Q, S, V, H))
+    if sections & {"vocab", "heads"}:
+        del Q, S
+        torch.cuda.empty_cache()
+    if "sampler" in sections:
+        res.update(sampler_rows(torch, qg, synth, dev))
+    return res
+
+
+def head_variants(torch, qg, synth, dev, Q, S, V, H):
+    res = {}
 
     # lm_head variants: the 40,960-row draft head gathered once from the same
     # table (copies rotated: 210 MB would otherwise stay in the Infinity Cache)
@@ -363,8 +398,6 @@ def extras(torch, qg, synth, np, dev):
     D, Md = dcfg["D"], dcfg["M"]
     dids = torch.from_numpy(synth.draft_ids(D, V, dcfg["seed"])).to(dev)
     DQ, DS = Q.index_select(0, dids).contiguous(), S.index_select(0, dids).contiguous()
-    del Q, S, y
-    torch.cuda.empty_cache()
     ncopy = copies_for(DQ.numel() + DS.numel() * 2)
     dcopies = [(DQ, DS)] + [(DQ.clone(), DS.clone()) for _ in range(ncopy - 1)]
     xd = torch.from_numpy(synth.acts(Md, H, dcfg["sigma"], dcfg["p"], dcfg["factor"], dcfg["seed"] + 100)).to(dev)
@@ -376,6 +409,7 @@ def extras(torch, qg, synth, np, dev):
                                       frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), weight_copies=ncopy)
     del dcopies, DQ, DS
     torch.cuda.empty_cache()
+    print("# bench: draft_head_w8a16_m1 measured", file=sys.stderr, flush=True)
 
     # ... and an int4 head (W4A16 over all 248,320 rows), at verify and batch M
     wcfg = synth.CONFIGS["lm_head_w4a16"]
@@ -394,9 +428,14 @@ def extras(torch, qg, synth, np, dev):
         res[f"lm_head_w4a16_m{M}"] = dict(M=M, K=K, N=N, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
                                           frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4),
                                           TFLOPS=round(2 * M * N * K / us / 1e6, 2), weight_copies=ncopy)
+        print(f"# bench: lm_head_w4a16_m{M} measured", file=sys.stderr, flush=True)
     del wcopies, wp, sp
     torch.cuda.empty_cache()
+    return res
 
+
+def sampler_rows(torch, qg, synth, dev):
+    res = {}
     # top-k / top-p sampler over the logit rows (copies rotated past the
     # Infinity Cache); bytes: the logits once, the outputs
     scfg = synth.CONFIGS["sampler"]
@@ -419,6 +458,7 @@ def extras(torch, qg, synth, np, dev):
                                              frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), logit_copies=ncopy)
         del lcopies, xs_d, ws
         torch.cuda.empty_cache()
+        print(f"# bench: sampler_r{R}_v{V}_k{k} measured", file=sys.stderr, flush=True)
     return res
 
 
