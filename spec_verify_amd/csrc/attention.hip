@@ -31,7 +31,14 @@ namespace {
 
 constexpr int kD = 256;           // head dimension
 constexpr int kBlk = 32;          // positions per staged block
-constexpr int kVtStride = 36;     // halves per transposed-V row (32 positions + 4): conflict-free 8-byte reads
+constexpr int kVtStride = 36;     // halves per transposed-V row (32 positions + 4)
+
+// Transposed V in LDS: dimension d's 32 positions form 8 groups of 4
+// consecutive positions (8 bytes); group j is stored at slot j ^ ((d / 16) % 8)
+// of row d.  The matrix-core reads (16 consecutive dimensions, 4 groups) and
+// the staging writes (dimensions 8 apart, one group) then fall in distinct
+// bank groups.
+__device__ __forceinline__ int vt_at(int d, int group) { return d * kVtStride + 4 * (group ^ ((d >> 4) & 7)); }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -91,34 +98,41 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
 
   const uint16_t* kbase = p.k + (int64_t)kvh * kD;
   const uint16_t* vbase = p.v + (int64_t)kvh * kD;
-  // K and V of a block: thread tid holds pieces tid + 256 pass (position
-  // pass * 8 + tid / 32, dims 8 (tid % 32) ..).  The next block's are loaded
-  // into registers while the current one is multiplied.
+  // K and V of a block: thread tid holds the 16-byte piece tid % 32 (dims
+  // 8 (tid % 32) ..) of positions 4 (tid / 32) + pass, pass = 0..3, so its
+  // four V pieces hold 4 consecutive positions of 8 dimensions.  The next
+  // block's are loaded into registers while the current one is multiplied.
+  const int kpiece = tid & 31, pgrp = tid >> 5;
   uint4 kreg[4], vreg[4];
   auto fetch = [&](int b0) {
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
-      const int idx = pass * 256 + tid, pos = b0 + (idx >> 5), piece = idx & 31;
+      const int pos = b0 + 4 * pgrp + pass;
       kreg[pass] = vreg[pass] = make_uint4(0, 0, 0, 0);
       if (pos < p_end) {
-        kreg[pass] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * rowstride + 8 * piece);
-        vreg[pass] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * rowstride + 8 * piece);
+        kreg[pass] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * rowstride + 8 * kpiece);
+        vreg[pass] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * rowstride + 8 * kpiece);
       }
     }
   };
   fetch(p_begin);
   for (int b0 = p_begin; b0 < p_end; b0 += kBlk) {
     __syncthreads();                                   // previous block's LDS reads are done
-    // K row-major (swizzled), V transposed, for positions b0 .. b0 + 31
+    // K row-major (swizzled), V transposed, for positions b0 .. b0 + 31:
+    // each of the thread's 8 dimensions gets its 4 positions in one 8-byte store
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int idx = pass * 256 + tid, pr = idx >> 5, piece = idx & 31;
-      k_lds[swz(pr, piece)] = kreg[pass];
-      const uint32_t w[4] = {vreg[pass].x, vreg[pass].y, vreg[pass].z, vreg[pass].w};
+    for (int pass = 0; pass < 4; ++pass) k_lds[swz(4 * pgrp + pass, kpiece)] = kreg[pass];
+    {
+      const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
+                                {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
+                                {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
+                                {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt_lds[(8 * piece + 2 * e) * kVtStride + pr] = (uint16_t)(w[e] & 0xFFFFu);
-        vt_lds[(8 * piece + 2 * e + 1) * kVtStride + pr] = (uint16_t)(w[e] >> 16);
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const uint32_t h0 = (w[0][e >> 1] >> sh) & 0xFFFFu, h1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h2 = (w[2][e >> 1] >> sh) & 0xFFFFu, h3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<uint2*>(&vt_lds[vt_at(8 * kpiece + e, pgrp)]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
       }
     }
     if (b0 + kBlk < p_end) fetch(b0 + kBlk);            // uniform
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
         f32x4 c = acc[i][d] * alpha;
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
-          const uint2 raw = *reinterpret_cast<const uint2*>(&vt_lds[(16 * d + col) * kVtStride + 16 * pt + 4 * quad]);
+          const uint2 raw = *reinterpret_cast<const uint2*>(&vt_lds[vt_at(16 * d + col, 4 * pt + quad)]);
           const f16x4 av = __builtin_bit_cast(f16x4, raw);
           c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pv[pt], c, 0, 0, 0);
         }
