@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     for (int d = 0; d < 16; ++d) acc[i][d] = (f32x4)0.0f;
   }
   const float kScale = 1.4426950408889634f / 16.0f;   // log2(e) / sqrt(256)
+  constexpr float kLazy = 8.0f;                        // exponentials below 2^8 (fp16 P)
 
   const uint16_t* kbase = p.k + (int64_t)kvh * kD;
   const uint16_t* vbase = p.v + (int64_t)kvh * kD;
@@ -173,9 +174,19 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
         }
       bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      const float m_new = fmaxf(m_run[i], bmax);
+      // The reference maximum of a row moves only when some row of the wave
+      // sees a block maximum more than kLazy above its own: otherwise the
+      // exponentials stay below 2^kLazy and the running output is not
+      // rescaled (a row's first finite block always moves it).
+      const bool rescale = __ballot(bmax > m_run[i] + kLazy) != 0;   // wave-uniform
+      float m_new = m_run[i], alpha = 1.0f;
+      if (rescale) {
+        m_new = fmaxf(m_run[i], bmax);
+        alpha = m_new > -__builtin_inff() ? __builtin_amdgcn_exp2f(m_run[i] - m_new) : 1.0f;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) acc[i][d] = acc[i][d] * alpha;
+      }
       const bool any = m_new > -__builtin_inff();
-      const float alpha = any ? __builtin_amdgcn_exp2f(m_run[i] - m_new) : 1.0f;
       float psum = 0.0f;
       f16x4 pv[2];
 #pragma unroll
@@ -190,10 +201,10 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
       psum += __shfl_xor(psum, 32, 64);
       l_run[i] = l_run[i] * alpha + psum;
       m_run[i] = m_new;
-      // O^T[dim][row] = alpha O^T + V^T P^T over the block's two position tiles
+      // O^T[dim][row] += V^T P^T over the block's two position tiles
 #pragma unroll
       for (int d = 0; d < 16; ++d) {
-        f32x4 c = acc[i][d] * alpha;
+        f32x4 c = acc[i][d];
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) {
           const uint2 raw = *reinterpret_cast<const uint2*>(&vt_lds[vt_at(16 * d + col, 4 * pt + quad)]);
@@ -225,24 +236,39 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
 }
 
 // Pass 2: one workgroup of 256 threads (one per dimension) per (KV head, row).
-// The splits' maxima and sums go to LDS first; each thread then reads its
-// dimension of every split's row, 16 loads in flight at a time.
+// Thread s < S takes split s's maximum and sum: the maximum over the splits
+// and the normaliser sum_s 2^(m_s - M) l_s are workgroup reductions, and the
+// weights 2^(m_s - M) go to LDS.  Each thread then adds its dimension of
+// every split's row in split order, 16 loads in flight at a time.
 constexpr int kMaxSplits = 256;   // attn_plan never makes more
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
-  const int kvh = blockIdx.y, row = blockIdx.x, dim = threadIdx.x;
-  __shared__ float ml[2 * kMaxSplits];
-  for (int i = dim; i < 2 * p.S; i += 256) ml[i] = p.ws_ml[(((int64_t)(i >> 1) * p.Hkv + kvh) * p.R + row) * 2 + (i & 1)];
-  __syncthreads();
-  float M = -__builtin_inff();
-  for (int s = 0; s < p.S; ++s) M = fmaxf(M, ml[2 * s]);
-  float num = 0.0f, den = 0.0f;
-#pragma unroll 16
-  for (int s = 0; s < p.S; ++s) {
-    const float ms = ml[2 * s];
-    const float w = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
-    den += w * ml[2 * s + 1];
-    num += w * p.ws_o[(((int64_t)s * p.Hkv + kvh) * p.R + row) * kD + dim];
+  const int kvh = blockIdx.y, row = blockIdx.x, dim = threadIdx.x, lane = dim & 63, wave = dim >> 6;
+  __shared__ float wts[kMaxSplits];
+  __shared__ float part[4];
+  float ms = -__builtin_inff(), ls = 0.0f;
+  if (dim < p.S) {
+    const float2 v = *reinterpret_cast<const float2*>(p.ws_ml + (((int64_t)dim * p.Hkv + kvh) * p.R + row) * 2);
+    ms = v.x;
+    ls = v.y;
   }
+  float M = wave_max(ms);
+  if (lane == 0) part[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  const float w = ms > -__builtin_inff() ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+  if (dim < p.S) wts[dim] = w;
+  float den = w * ls;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+  __syncthreads();                                   // part[] reads done, wts[] written
+  if (lane == 0) part[wave] = den;
+  __syncthreads();
+  den = (part[0] + part[1]) + (part[2] + part[3]);
+  float num = 0.0f;
+  const float* src = p.ws_o + ((int64_t)kvh * p.R + row) * kD + dim;
+  const int64_t sstride = (int64_t)p.Hkv * p.R * kD;        // between splits
+#pragma unroll 16
+  for (int s = 0; s < p.S; ++s) num += wts[s] * src[s * sstride];
   const int t = row / p.G, h = kvh * p.G + row % p.G;
   p.o[((int64_t)t * p.Hq + h) * kD + dim] = float_to_half_bits(num / den);
 }
