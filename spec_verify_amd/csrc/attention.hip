@@ -57,6 +57,104 @@ struct AttnParams {
 // hit 16 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int piece) { return row * 32 + (piece ^ (row & 15)); }
 
+// V pieces of 4 consecutive positions (group g of the block) for dims
+// 8 piece .. 8 piece + 7, transposed into the LDS layout: one 8-byte store
+// per dimension.
+__device__ __forceinline__ void stage_v(uint16_t* vt_lds, const uint4* v, int piece, int g) {
+  const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w},
+                            {v[1].x, v[1].y, v[1].z, v[1].w},
+                            {v[2].x, v[2].y, v[2].z, v[2].w},
+                            {v[3].x, v[3].y, v[3].z, v[3].w}};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int sh = 16 * (e & 1);
+    const uint32_t h0 = (w[0][e >> 1] >> sh) & 0xFFFFu, h1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
+    const uint32_t h2 = (w[2][e >> 1] >> sh) & 0xFFFFu, h3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
+    *reinterpret_cast<uint2*>(&vt_lds[vt_at(8 * piece + e, g)]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  }
+}
+
+// One 32-position block for one 16-row m-tile of the split: scores from the
+// staged K (S^T = K Q^T, a lane holding 4 positions of row mt*16 + col), the
+// online softmax update of the row's maximum, sum and output, and
+// O^T += V^T P^T from the staged transposed V.
+__device__ __forceinline__ void attn_tile_block(const AttnParams& p, const uint4* q_lds, const uint4* k_lds,
+                                                const uint16_t* vt_lds, int b0, int p_end, int mt, int col, int quad,
+                                                f32x4 (&acc)[16], float& m_run, float& l_run) {
+  const float kScale = 1.4426950408889634f / 16.0f;   // log2(e) / sqrt(256)
+  constexpr float kLazy = 8.0f;                        // exponentials below 2^8 (fp16 P)
+  const int row = mt * 16 + col;
+  const int t = row / p.G;
+  const int last = p.L - p.T + t;              // last position query t sees
+  // scores for the block: two 16-position tiles, lane = (row col, positions 4 quad ..)
+  f32x4 s[2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt) {
+    f32x4 c = (f32x4)0.0f;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      const int piece = 4 * sl + quad;
+      const f16x8 a = __builtin_bit_cast(f16x8, k_lds[swz(16 * pt + col, piece)]);
+      const f16x8 bq = __builtin_bit_cast(f16x8, q_lds[swz(row, piece)]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, c, 0, 0, 0);
+    }
+    s[pt] = c;
+  }
+  // The S^T tile has positions in rows (4 quad + j) and query rows in
+  // columns (col): lane holds s(row = mt*16 + col, pos = b0 + 16 pt + 4 quad + j).
+  float bmax = -__builtin_inff();
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = b0 + 16 * pt + 4 * quad + j;
+      const bool ok = row < p.R && pos < p_end && pos <= last;
+      s[pt][j] = ok ? s[pt][j] * kScale : -__builtin_inff();
+      bmax = fmaxf(bmax, s[pt][j]);
+    }
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+  // The reference maximum of a row moves only when some row of the wave
+  // sees a block maximum more than kLazy above its own: otherwise the
+  // exponentials stay below 2^kLazy and the running output is not
+  // rescaled (a row's first finite block always moves it).
+  const bool rescale = __ballot(bmax > m_run + kLazy) != 0;   // wave-uniform
+  float m_new = m_run, alpha = 1.0f;
+  if (rescale) {
+    m_new = fmaxf(m_run, bmax);
+    alpha = m_new > -__builtin_inff() ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = acc[d] * alpha;
+  }
+  const bool any = m_new > -__builtin_inff();
+  float psum = 0.0f;
+  f16x4 pv[2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = any ? __builtin_amdgcn_exp2f(s[pt][j] - m_new) : 0.0f;
+      psum += e;
+      pv[pt][j] = (_Float16)e;
+    }
+  psum += __shfl_xor(psum, 16, 64);
+  psum += __shfl_xor(psum, 32, 64);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  // O^T[dim][row] += V^T P^T over the block's two position tiles
+#pragma unroll
+  for (int d = 0; d < 16; ++d) {
+    f32x4 c = acc[d];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(&vt_lds[vt_at(16 * d + col, 4 * pt + quad)]);
+      const f16x4 av = __builtin_bit_cast(f16x4, raw);
+      c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pv[pt], c, 0, 0, 0);
+    }
+    acc[d] = c;
+  }
+}
+
 template <int MTW>
 __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
@@ -94,9 +192,6 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
 #pragma unroll
     for (int d = 0; d < 16; ++d) acc[i][d] = (f32x4)0.0f;
   }
-  const float kScale = 1.4426950408889634f / 16.0f;   // log2(e) / sqrt(256)
-  constexpr float kLazy = 8.0f;                        // exponentials below 2^8 (fp16 P)
-
   const uint16_t* kbase = p.k + (int64_t)kvh * kD;
   const uint16_t* vbase = p.v + (int64_t)kvh * kD;
   // K and V of a block: thread tid holds the 16-byte piece tid % 32 (dims
@@ -123,19 +218,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     // each of the thread's 8 dimensions gets its 4 positions in one 8-byte store
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) k_lds[swz(4 * pgrp + pass, kpiece)] = kreg[pass];
-    {
-      const uint32_t w[4][4] = {{vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w},
-                                {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w},
-                                {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w},
-                                {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w}};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        const uint32_t h0 = (w[0][e >> 1] >> sh) & 0xFFFFu, h1 = (w[1][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h2 = (w[2][e >> 1] >> sh) & 0xFFFFu, h3 = (w[3][e >> 1] >> sh) & 0xFFFFu;
-        *reinterpret_cast<uint2*>(&vt_lds[vt_at(8 * kpiece + e, pgrp)]) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-      }
-    }
+    stage_v(vt_lds, vreg, kpiece, pgrp);
     if (b0 + kBlk < p_end) fetch(b0 + kBlk);            // uniform
     __syncthreads();
 
@@ -143,76 +226,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnParams p) {
     for (int i = 0; i < MTW; ++i) {
       const int mt = wave + 4 * i;
       if (mt >= MT) break;                             // uniform per wave
-      const int row = mt * 16 + col;
-      const int t = row / p.G;
-      const int last = p.L - p.T + t;                  // last position query t sees
-      // scores for the block: two 16-position tiles, lane = (row col, positions 4 quad ..)
-      f32x4 s[2];
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        f32x4 c = (f32x4)0.0f;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int piece = 4 * sl + quad;
-          const f16x8 a = __builtin_bit_cast(f16x8, k_lds[swz(16 * pt + col, piece)]);
-          const f16x8 bq = __builtin_bit_cast(f16x8, q_lds[swz(row, piece)]);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, c, 0, 0, 0);
-        }
-        s[pt] = c;
-      }
-      // The S^T tile has positions in rows (4 quad + j) and query rows in
-      // columns (col): lane holds s(row = mt*16 + col, pos = b0 + 16 pt + 4 quad + j).
-      float bmax = -__builtin_inff();
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int pos = b0 + 16 * pt + 4 * quad + j;
-          const bool ok = row < p.R && pos < p_end && pos <= last;
-          s[pt][j] = ok ? s[pt][j] * kScale : -__builtin_inff();
-          bmax = fmaxf(bmax, s[pt][j]);
-        }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-      // The reference maximum of a row moves only when some row of the wave
-      // sees a block maximum more than kLazy above its own: otherwise the
-      // exponentials stay below 2^kLazy and the running output is not
-      // rescaled (a row's first finite block always moves it).
-      const bool rescale = __ballot(bmax > m_run[i] + kLazy) != 0;   // wave-uniform
-      float m_new = m_run[i], alpha = 1.0f;
-      if (rescale) {
-        m_new = fmaxf(m_run[i], bmax);
-        alpha = m_new > -__builtin_inff() ? __builtin_amdgcn_exp2f(m_run[i] - m_new) : 1.0f;
-#pragma unroll
-        for (int d = 0; d < 16; ++d) acc[i][d] = acc[i][d] * alpha;
-      }
-      const bool any = m_new > -__builtin_inff();
-      float psum = 0.0f;
-      f16x4 pv[2];
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = any ? __builtin_amdgcn_exp2f(s[pt][j] - m_new) : 0.0f;
-          psum += e;
-          pv[pt][j] = (_Float16)e;
-        }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run[i] = l_run[i] * alpha + psum;
-      m_run[i] = m_new;
-      // O^T[dim][row] += V^T P^T over the block's two position tiles
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        f32x4 c = acc[i][d];
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          const uint2 raw = *reinterpret_cast<const uint2*>(&vt_lds[vt_at(16 * d + col, 4 * pt + quad)]);
-          const f16x4 av = __builtin_bit_cast(f16x4, raw);
-          c = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pv[pt], c, 0, 0, 0);
-        }
-        acc[i][d] = c;
-      }
+      attn_tile_block(p, q_lds, k_lds, vt_lds, b0, p_end, mt, col, quad, acc[i], m_run[i], l_run[i]);
     }
   }
 
