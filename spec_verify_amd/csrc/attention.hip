@@ -296,7 +296,8 @@ AttnPlan attn_plan(int64_t T, int64_t Hq, int64_t Hkv, int64_t L) {
   // at least one block).  Short caches get as many splits as they have
   // blocks: at 1.5k positions, 48 splits of one block ran in 14.6 us, 12
   // splits of four in 20.9 us (the per-split partial rows then outweigh the
-  // cache, but pass 1 fills the GPU).  More than 256 workgroups made long
+  // cache, but pass 1 fills the GPU); with the current pass 1, 24 splits of
+  // two took 13.5 us and 16 of three 12.5 us, against 12.6 us.  More than 256 workgroups made long
   // caches slower (16k positions: 44 us at 512 against 38 us), as pass 2
   // has more partial rows to read.
   int64_t S = std::max<int64_t>(1, std::min<int64_t>((256 + Hkv - 1) / Hkv, (L + kBlk - 1) / kBlk));
