@@ -161,17 +161,19 @@ int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, co
  *   x         fp16 [M][ldx] (first H columns used), ldx >= H, ldx % 8 == 0
  *   w         fp16 [H], the norm's weight
  *   eps       >= 0, finite
- *   y         fp16 [M][H] out, contiguous, or NULL to skip it
- *             y[m][h] = fp16((fp32(x[m][h]) * r[m]) * fp32(w[h])), with
- *             r[m] = 1 / sqrt(ss[m] / H + eps) in IEEE fp32 (division, square
- *             root, division; r = 0 where ss / H + eps == 0) and ss[m] the
- *             fp32 sum of x[m][h]^2 as a binary tree over the row zero-padded
- *             to a power of two (adjacent entries pairwise, level by level)
+ *   y         fp16 [M][H] out, contiguous, or NULL to skip it:
+ *             y[m][h] = x[m][h] * w[h] / sqrt(sum_h' x[m][h']^2 / H + eps)
+ *             rounded to fp16, evaluated in fp32 (a tree-ordered sum of
+ *             squares, IEEE division and square root, (x * r) * w; y = 0
+ *             where sum / H + eps == 0).  Within one fp16 unit in the last
+ *             place of the correctly rounded value, and equal to it except
+ *             where the exact value lies within a few fp32 ulps of a point
+ *             halfway between two fp16 numbers.
  *   prepared  out, prepared_bytes >= w4a8_prepared_bytes(M, H): exactly what
- *             w4a8_prepare writes for y (codes and token scales of
- *             act_quant_int8 on y), for w4a8_gemm_prepared with K = H
- *   H % 128 == 0, H <= 65536.  y and the codes are bit-exact against that
- *   definition.  One kernel launch.
+ *             w4a8_prepare writes for that y (codes and token scales of
+ *             act_quant_int8 on the y this call computes, bit-exact), for
+ *             w4a8_gemm_prepared with K = H
+ *   H % 128 == 0, H <= 65536.  One kernel launch.
  */
 int rmsnorm_w4a8_prepare(const void* x_f16, const void* w_f16, int64_t M, int64_t H, int64_t ldx, float eps,
                          void* y_f16, void* prepared, size_t prepared_bytes, void* stream);
@@ -231,8 +233,10 @@ int sample_topk_topp(const void* logits_f16, int64_t R, int64_t V, int64_t ld, i
 
 /*
  * w4a8_gemm_debug -- w4a8_gemm that also exposes its integer stages, for
- * bit-exact checks.  Runs the same kernels as w4a8_gemm and in addition
- * writes
+ * bit-exact checks.  For every M it runs the kernels w4a8_gemm runs (the
+ * quantiser, then the same GEMM kernel with the same work split, compiled
+ * with stores of the group partials), so y is bit-identical to w4a8_gemm's,
+ * and in addition writes
  *   q_out     int8 [M][K]   the activation codes   (may be NULL)
  *   scale_out fp32 [M]      the token scales       (may be NULL)
  *   partials  int32 [m1-m0][n1-n0][K/128]  P[m][n][g] for m0 <= m < m1,
@@ -284,6 +288,20 @@ int embed_gather_dequant_int8(const int32_t* ids, int64_t T, const int8_t* table
  */
 int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H,
                      int8_t* Q, void* S_f16, void* stream);
+
+/*
+ * qg_selftest_quant_division -- exhaustive device check of the quantiser's
+ * division ([OPT] "In full" item 4: per-token int8 activations; codes are
+ * rint(x / scale) with scale = absmax / 127).  The kernels form x / scale as
+ * a reciprocal product with one correction step instead of a division per
+ * element; this runs that step beside the IEEE division for every finite
+ * positive fp16 absmax and every fp16 x with |x| <= absmax (1,007,713,278
+ * pairs) and adds, to the caller's zero-initialised device counters,
+ *   counts[0]  the pairs checked
+ *   counts[1]  the pairs where the two rounded quotients differ
+ * counts: 2 x uint64, 8-byte aligned device memory.  One kernel launch.
+ */
+int qg_selftest_quant_division(unsigned long long* counts, void* stream);
 
 #ifdef __cplusplus
 }

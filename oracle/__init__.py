@@ -35,9 +35,10 @@ zero rows.
 Parity pins: every function below is pinned in ``tests/test_oracle_*.py`` by
 brute force with exact rationals, closed forms and invariants.  One step has
 no page behind it: ``rmsnorm`` (the norm whose output the fused quantiser
-takes; the pages name no norm).  Its definition is a reading, pinned by
-closed forms, an exact scale invariance and a float64 bound, and is marked
-"parity unpinned" as to the pages.
+takes; the pages name no norm).  Its definition is a reading (the float64
+value rounded once to fp16), pinned by a 60-digit decimal evaluation,
+closed forms and an exact scale invariance, and is marked "parity unpinned"
+as to the pages.
 """
 from __future__ import annotations
 
@@ -48,7 +49,7 @@ GROUP = 128
 __all__ = [
     "GROUP", "quant_act", "partials", "ref_w4a8", "ref_w4a16", "quant_table",
     "ref_gather", "ref_w8a16", "fp16_bounds", "FP16_MAX_RATIO", "FP16_FROB",
-    "tree_sum_f32", "rmsnorm_factor", "rmsnorm_f32", "rmsnorm", "rmsnorm_quant", "ref_verify_attention",
+    "rmsnorm", "rmsnorm_quant", "ref_verify_attention",
     "topk_topp_sample",
 ]
 
@@ -84,59 +85,34 @@ def quant_act(x):
     return q, s
 
 
-def tree_sum_f32(v):
-    """Row sums of a float32 matrix as a binary tree: the row is zero-padded
-    to a power-of-two length, then adjacent entries are added pairwise,
-    level by level, in float32.  (Padding further only adds zero subtrees,
-    which leave every sum unchanged, so the power chosen does not matter.)"""
-    v = np.asarray(v, dtype=np.float32)
-    M, n = v.shape
-    p = 1
-    while p < n:
-        p *= 2
-    t = np.zeros((M, p), np.float32)
-    t[:, :n] = v
-    while t.shape[1] > 1:
-        t = t[:, 0::2] + t[:, 1::2]
-    return t[:, 0]
-
-
-def rmsnorm_factor(x, eps):
-    """The per-row factor r of ``rmsnorm`` (float32 [M]): for row m of length H
-        ss[m] = tree_sum_f32(fp32(x[m, :]) ** 2)   (each square is exact)
-        t[m]  = ss[m] / H + eps                    (IEEE fp32 division, then add)
-        r[m]  = 1 / sqrt(t[m])                     (IEEE fp32 sqrt, then division)
-    and r = 0 for a row with t == 0 (all zeros, eps == 0)."""
-    xf = np.asarray(x, dtype=np.float16).astype(np.float32)
-    M, H = xf.shape
-    r = np.zeros(M, np.float32)
-    if M == 0:
-        return r
-    ss = tree_sum_f32(xf * xf)
-    t = ss / np.float32(H) + np.float32(eps)
-    pos = t > 0
-    r[pos] = np.float32(1.0) / np.sqrt(t[pos])
-    return r
-
-
-def rmsnorm_f32(x, w, eps):
-    """The float32 values rmsnorm rounds to fp16: (fp32(x[m, h]) * r[m]) * fp32(w[h])."""
-    xf = np.asarray(x, dtype=np.float16).astype(np.float32)
-    wf = np.asarray(w, dtype=np.float16).astype(np.float32)
-    r = rmsnorm_factor(x, eps)
-    return (xf * r[:, None]) * wf[None, :]
-
-
 def rmsnorm(x, w, eps):
-    """RMSNorm of fp16 rows with an fp16 weight, all in float32.
+    """RMSNorm of fp16 rows with an fp16 weight, rounded once to fp16.
 
     Parity unpinned as to the pages, which name no norm: this is the plain
-    reading of the norm whose output a fused quantiser would take.
-        y[m, h] = fp16((fp32(x[m, h]) * r[m]) * fp32(w[h]))
-    with r from ``rmsnorm_factor`` (a root-mean-square over the row, by a
-    float32 binary-tree sum).  Returns y as float16 [M, H].
+    reading of the norm whose output a fused quantiser would take.  For row
+    m of length H,
+        ss[m]   = sum_h x[m, h]^2                  (exactly rounded: math.fsum)
+        r[m]    = 1 / sqrt(ss[m] / H + eps)        (float64, eps as fp32; r = 0 where that is 0)
+        y[m, h] = fp16(x[m, h] * r[m] * w[h])      (float64 product, one rounding to fp16)
+    Every float64 step is within a few units of 2^-53 of the exact value, so
+    y is the correctly rounded fp16 of x * w / sqrt(mean(x^2) + eps) except
+    where that value lies within about 1e-15 (relative) of a point halfway
+    between two fp16 numbers.  No summation order is part of the definition:
+    any evaluation close enough to the exact value is a correct reading.
+    Returns y as float16 [M, H].
     """
-    return rmsnorm_f32(x, w, eps).astype(np.float16)
+    import math
+    xf = np.asarray(x, dtype=np.float16).astype(np.float64)
+    wf = np.asarray(w, dtype=np.float16).astype(np.float64)
+    M, H = xf.shape
+    e = float(np.float32(eps))                      # eps is an fp32 argument
+    y = np.zeros((M, H), np.float64)
+    for m in range(M):
+        ss = math.fsum((xf[m] * xf[m]).tolist())    # squares of fp16 values are exact in float64
+        t = ss / H + e
+        if t > 0:
+            y[m] = xf[m] * (1.0 / math.sqrt(t)) * wf
+    return y.astype(np.float16)
 
 
 def rmsnorm_quant(x, w, eps):

@@ -10,9 +10,9 @@ Entry points (see ``include/qgemm.h`` for the contract of each):
 act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare, rmsnorm_w4a8_prepare,
 verify_attention_f16, sample_topk_topp,
 w4a8_gemm_prepared, w4a8_gemm_debug,
-w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, plus the size
-helpers w4_packed_bytes, w4_scales_bytes, qg_workspace_bytes and
-qg_status_string.
+w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, the self-test
+qg_selftest_quant_division, plus the size helpers w4_packed_bytes,
+w4_scales_bytes, qg_workspace_bytes and qg_status_string.
 """
 from __future__ import annotations
 
@@ -65,6 +65,7 @@ _SIGS = {
     "w8a16_gemm": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]),
     "embed_gather_dequant_int8": (ctypes.c_int, [_p, _i64, _p, _p, _i64, _i64, _p, _p]),
     "quant_table_int8": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
+    "qg_selftest_quant_division": (ctypes.c_int, [_p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -312,3 +313,14 @@ def quant_table_int8(src_bf16, Q=None, S=None):
     _check("quant_table_int8", lib.quant_table_int8(_ptr(src_bf16), V, H, _ptr(Q), _ptr(S),
                                                     _stream(src_bf16.device)))
     return Q, S
+
+
+def qg_selftest_quant_division(device=None):
+    """Run the library's exhaustive check of the quantiser's division on the
+    device; returns (pairs checked, pairs whose rounded quotients differ)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    counts = torch.zeros((2,), dtype=torch.int64, device=dev)
+    _check("qg_selftest_quant_division", lib.qg_selftest_quant_division(_ptr(counts), _stream(dev)))
+    c = counts.cpu()
+    return int(c[0]), int(c[1])

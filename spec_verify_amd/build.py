@@ -18,7 +18,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemm.so")
 
 SOURCES = ["act_quant.hip", "repack.hip", "gemm_skinny.hip", "gemm_wide.hip", "gemm_w4a8_large.hip", "embed.hip",
-           "attention.hip", "sampler.hip", "api.cpp"]
+           "attention.hip", "sampler.hip", "selftest.hip", "api.cpp"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -11,12 +11,13 @@
 // give each a few 16-byte chunks; rows longer than the register budget are
 // re-read (from cache) in the quantise pass.
 //
-// Division.  The quotient x / scale is formed without a divide per element:
-// with r = 1 / scale (one IEEE division per thread), y0 = x * r,
-// e = fma(-y0, scale, x) (exact residual) and y1 = fma(e, r, y0).  Markstein's
-// correction step makes y1 the correctly rounded quotient here; an exhaustive
-// run over every finite fp16 absmax and every fp16 x with |x| <= absmax
-// (1,007,713,278 pairs) gave rint(y1) == rint(x / scale) in all of them.
+// Division.  The quotient x / scale is formed without a divide per element
+// (corrected_quotient in quant_math.h): one IEEE division per thread for
+// r = 1 / scale, then a product and Markstein's correction step.  The
+// library's self-test qg_selftest_quant_division runs every finite fp16
+// absmax against every fp16 x with |x| <= absmax (1,007,713,278 pairs) and
+// counts the pairs where rint of that quotient differs from rint of the
+// IEEE quotient x / scale; a GPU test requires the count to be zero.
 //
 // Output orders.  Row-major q[m][k], and/or the "fragment" order the
 // weight-streaming W4A8 GEMM loads: rows in tiles of 16, and for tile mt,
@@ -29,6 +30,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "quant_math.h"
 
 namespace qg {
 namespace {
@@ -45,11 +47,7 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
 
 // rint(x / s) clamped to [-127, 127], with rs = 1 / s (see "Division").
 __device__ __forceinline__ int quant1(uint32_t hbits, float s, float rs) {
-  const float x = half_bits_to_float(hbits);
-  const float y0 = x * rs;
-  const float e = __builtin_fmaf(-y0, s, x);
-  const float y1 = __builtin_fmaf(e, rs, y0);
-  return (int)fminf(fmaxf(rintf(y1), -127.0f), 127.0f);
+  return (int)fminf(fmaxf(rintf(corrected_quotient(half_bits_to_float(hbits), s, rs)), -127.0f), 127.0f);
 }
 
 __device__ __forceinline__ uint2 quant8(uint4 v, float s, float rs) {
@@ -132,18 +130,22 @@ __global__ __launch_bounds__(1024) void act_quant_kernel(const uint16_t* __restr
 // RMSNorm fused with the quantiser: the norm's fp16 output y is quantised per
 // row exactly as above (its codes and scale are those of act_quant on y).
 //
-// The norm, per row of length H, all in fp32:
-//   ss = sum of x[h]^2 as a binary tree over the row zero-padded to a power
-//        of two (adjacent entries pairwise, level by level; squares of fp16
-//        values are exact in fp32, and adding zero subtrees changes nothing)
+// The norm is y = x * w / sqrt(mean(x^2) + eps), rounded to fp16.  Here it
+// is evaluated in fp32, per row of length H:
+//   ss = sum of x[h]^2 (squares of fp16 values are exact in fp32), added as
+//        a binary tree: relative error at most log2(H) * 2^-24
 //   r  = 1 / sqrt(ss / H + eps)   (IEEE division, square root, division;
 //        r = 0 when ss / H + eps == 0)
 //   y  = fp16((x * r) * w)
-// The tree is formed by the thread layout: chunk c (8 values, itself summed as
-// a 3-level tree) belongs to thread c % T in slot c / T; lanes then add by
-// xor-shuffles (aligned blocks of 2, 4, .., 64 lanes), waves pairwise
-// through LDS, and finally the MAXC slots pairwise.  T and MAXC are powers
-// of two with T * MAXC chunks >= the row.
+// so y is within one fp16 unit in the last place of the correctly rounded
+// value, and equal to it except where the exact value lies within a few
+// fp32 ulps of a point halfway between two fp16 numbers.  The tree follows
+// the thread layout: chunk c (8 values, itself summed as a 3-level tree)
+// belongs to thread c % T in slot c / T; lanes then add by xor-shuffles
+// (aligned blocks of 2, 4, .., 64 lanes), waves pairwise through LDS, and
+// finally the MAXC slots pairwise.  T and MAXC are powers of two with
+// T * MAXC chunks >= the row.  Any order would do; a tree keeps the error
+// bound logarithmic in H and every step free of atomics.
 // ---------------------------------------------------------------------------
 
 // Sum over a wave's lanes as a balanced binary tree over lane index: after

@@ -412,6 +412,12 @@ int embed_gather_dequant_int8(const int32_t* ids, int64_t T, const int8_t* table
                                          reinterpret_cast<uint16_t*>(out_f16), as_stream(stream)));
 }
 
+int qg_selftest_quant_division(unsigned long long* counts, void* stream) {
+  if (!counts || (reinterpret_cast<uintptr_t>(counts) & 7u)) return QG_ERR_INVALID_ARG;
+  clear_stale_error();
+  return launch_status(qg::launch_quant_division_check(counts, as_stream(stream)));
+}
+
 int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H, int8_t* Q, void* S_f16, void* stream) {
   if (V <= 0 || H <= 0) return QG_ERR_INVALID_ARG;
   if (H % kGroup || V > kMaxDim || H > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;

@@ -107,6 +107,10 @@ hipError_t launch_gather(const int32_t* ids, int64_t T, const int8_t* table, con
 hipError_t launch_quant_table(const uint16_t* src, int64_t V, int64_t H, int8_t* Q, uint16_t* S,
                               hipStream_t st);
 
+// Exhaustive check of the quantiser's division: adds the pairs checked to
+// counts[0] and the mismatches to counts[1].
+hipError_t launch_quant_division_check(unsigned long long* counts, hipStream_t st);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

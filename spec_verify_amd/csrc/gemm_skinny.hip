@@ -168,8 +168,8 @@ __device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs
 // power of two, so the result is the same as scaling every term).
 template <int MODE, int NT, int MT, bool DEBUG>
 __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage<MODE, NT, MT>& st, int g,
-                                              bool gvalid, int nt0, int mt0, int lane, const uint16_t* lds_s,
-                                              f32x4 (&acc)[NT][MT]) {
+                                              bool gvalid, int nt0, int nvalid, int mt0, int lane,
+                                              const uint16_t* lds_s, f32x4 (&acc)[NT][MT]) {
   const int col = lane & 15, quad = lane >> 4;
   const int gs = gvalid ? g : 0;
 #pragma unroll
@@ -193,8 +193,9 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[r], (float)sc[r], acc[j][mt][r]);
         if constexpr (DEBUG) {
+          // tiles past nvalid belong to the next n-block (zero weights here)
           const int m = (mt0 + mt) * 16 + col;
-          if (gvalid && m >= p.dm0 && m < p.dm1 && m < p.M) {
+          if (gvalid && j < nvalid && m >= p.dm0 && m < p.dm1 && m < p.M) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int n = (nt0 + j) * 16 + 4 * quad + r;
@@ -431,7 +432,7 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int ii = r * PF + s;
-      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), true, nt0, mt0, lane, lds_s, acc);
+      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), true, nt0, nvalid, mt0, lane, lds_s, acc);
       // Stages past the last group load nothing (out-of-range offsets) and
       // multiply zeros, which keeps this loop free of branches.
       load_stage<MODE, NT, MT>(p, rs, st[s], ii + PF < ng, gidx(ii + PF), lane, mt0);
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int ii = (rounds - 1) * PF + s;
-      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), ii < ng, nt0, mt0, lane, lds_s, acc);
+      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), ii < ng, nt0, nvalid, mt0, lane, lds_s, acc);
     }
   }
 
@@ -450,109 +451,8 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
   sum_and_store<MODE, NT, MT, NW>(p, acc, nt0, mt0, nvalid, wave, lane, red);
 }
 
-// W4A8 at decode size (32 < M <= 64, K <= 5120): everything in flight at
-// once.  In the kernel above each wave's weight loads (HBM latency) and
-// activation loads (L2 hits) share its in-order return queue, and its ring
-// pays the HBM latency once per refill.  Here a workgroup's whole weight and
-// scale slab (2 n-tiles x K/128 groups: at most 80 KiB + 2.5 KiB) moves to
-// LDS with LDS-direct loads, and every wave's activation codes for all of
-// its groups (at most GPW) move to registers, all issued up front; one wait
-// and one barrier later every operand is on the CU.  Groups, their order per
-// wave and the wave sums are those of the kernel above, so the two give
-// bit-identical rows.
-template <int MT, int GPW>
-__global__ __launch_bounds__(512) void decode_w4a8_kernel(SkinnyParams p) {
-  constexpr int NT = 2, NW = 8;
-  constexpr int SLAB = NT * NW * GPW;                 // 1 KiB weight blocks the LDS holds
-  constexpr int SBLK = (SLAB * 32 + 1023) / 1024;     // 1 KiB loads of the slab's scales
-  __shared__ __attribute__((aligned(16))) uint4 wl[SLAB * 64];
-  __shared__ __attribute__((aligned(16))) uint4 sl[SBLK * 64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, quad = lane >> 4;
-  const int nt0 = blockIdx.x * NT;
-  const int nvalid = min(NT, p.N / 16 - nt0);
-  const uint32_t G = (uint32_t)p.G;
-
-  // The slab is contiguous in both packed layouts: block (tile j, group g)
-  // at (j G + g) KiB, its 16 scales at (j G + g) * 32 B.
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(reinterpret_cast<const uint8_t*>(p.w) + (int64_t)nt0 * G * 1024, (uint32_t)(nvalid * G * 1024));
-  const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.s + (int64_t)nt0 * G * 16, (uint32_t)(nvalid * G * 32));
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.act, (uint32_t)((int64_t)((p.M + 15) / 16) * 16 * p.K));
-
-  const int ng = wave < p.G ? (p.G - wave + NW - 1) / NW : 0;
-  const int rot = ng > 0 ? (int)(blockIdx.x % (unsigned)ng) : 0;
-  auto gidx = [&](int i) { return wave + NW * (i < ng ? (i + rot < ng ? i + rot : i + rot - ng) : i); };
-
-  // Activation codes of this wave's groups, in fragment order (see
-  // act_quant.hip): one 1 KiB load per (m-tile, half of the group).
-  i32x4 x[GPW][MT][2];
-#pragma unroll
-  for (int i = 0; i < GPW; ++i) {
-    const uint32_t bad = i < ng ? 0u : kOOB;
-    const uint32_t g = (uint32_t)gidx(i);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t off = ((((uint32_t)mt * G + g) * 2u) * 64u + lane) * 16u + bad;
-      x[i][mt][0] = __builtin_bit_cast(i32x4, ld128(rx, off));
-      x[i][mt][1] = __builtin_bit_cast(i32x4, ld128(rx, off + 1024u));
-    }
-  }
-  // The slab: wave w fills blocks w, w + NW, ... (past the valid tiles the
-  // loads are out of range and store zeros), then the scales.
-#pragma unroll
-  for (int i = 0; i < NT * GPW; ++i) {
-    const int b = wave + NW * i;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)&wl[b * 64], 16, (uint32_t)(b * 1024 + lane * 16), 0, 0,
-                                             kAuxStream);
-  }
-  if (wave < SBLK)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (lds_ptr_t)&sl[wave * 64], 16, (uint32_t)(wave * 1024 + lane * 16), 0,
-                                             0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  f32x4 acc[NT][MT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = (f32x4)0.0f;
-  const uint16_t* sh = reinterpret_cast<const uint16_t*>(sl);
-#pragma unroll
-  for (int i = 0; i < GPW; ++i) {
-    // Stages past the wave's last group multiply zero codes (their
-    // activations were out-of-range loads); their LDS reads stay inside
-    // the slab (group index < NW * GPW).
-    const int g = gidx(i);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int blk = j * (int)G + g;
-      const uint4 wv = blk < SLAB ? wl[blk * 64 + lane] : make_uint4(0, 0, 0, 0);
-      const uint2 sv = blk < SLAB ? *reinterpret_cast<const uint2*>(sh + blk * 16 + 4 * quad) : make_uint2(0, 0);
-      const _Float16 sc[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sv.x & 0xFFFFu)),
-                              __builtin_bit_cast(_Float16, (uint16_t)(sv.x >> 16)),
-                              __builtin_bit_cast(_Float16, (uint16_t)(sv.y & 0xFFFFu)),
-                              __builtin_bit_cast(_Float16, (uint16_t)(sv.y >> 16))};
-      const i32x4 a0 = w4_to_i8x16(wv.x, wv.y);
-      const i32x4 a1 = w4_to_i8x16(wv.z, wv.w);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, x[i][mt][0], (i32x4)0, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, x[i][mt][1], P, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[r], (float)sc[r], acc[j][mt][r]);
-      }
-    }
-  }
-  (void)col;
-  __shared__ f32x4 red[red_bufs<NT, MT, NW>()][NW][red_chunk<NT, MT, NW>()][64];
-  sum_and_store<kW4A8, NT, MT, NW>(p, acc, nt0, 0, nvalid, wave, lane, red);
-}
-
-constexpr int kDecodeGPW = 5;   // groups per wave of decode_w4a8_kernel: K <= 8 * 5 * 128
-// W4A8 at 16 < M <= 64 when N / 16 is a multiple of 5: the streaming
-// kernel with the rows split over workgroups (see launch_skinny).
+// W4A8 at 16 < M <= 64: the streaming kernel with the rows split over
+// workgroups (see launch_skinny).
 constexpr int kMsplitNT = 5, kMsplitPF = 1;
 constexpr int kBalancedWgs = 512;   // two workgroups per CU
 
@@ -623,26 +523,26 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.dm0 = (int)a.dm0; p.dm1 = (int)a.dm1; p.dn0 = (int)a.dn0; p.dn1 = (int)a.dn1;
   p.ms = 1;
   p.wgs = 0;
-  // W4A8 at 16 < M <= 64 (decode batches): one 16-row m-tile and 5 n-tiles
-  // per workgroup, 8 waves splitting K, a one-stage ring.  Each CU then
-  // pulls 82 KB of activation codes and 200 KB of weights (most of them L2
-  // hits, shared by the n-block's m-groups on one XCD) instead of 327 KB of
-  // codes and 82 KB of weights, and the loads it keeps in flight stay few;
-  // the CU's limit on outstanding L2 requests is what bounds this GEMM.
-  // Measured at M = 64, K = N = 5120: 8.7 us, against 10.3 us for the
-  // LDS-slab kernel below and 10.9 us for two n-tiles x 64 rows.
-  if (a.mode == kW4A8 && a.dbg == nullptr && a.M > 16 && p.N / 16 <= 1024 && (p.N / 16) % kMsplitNT == 0) {
+  // W4A8 at 16 < M <= 64 (decode batches): one 16-row m-tile and at most
+  // 5 n-tiles per workgroup (the n-tiles dealt into ceil(T / 5) balanced
+  // blocks of 4 or 5), 8 waves splitting K, a one-stage ring.  Each CU then
+  // pulls 82 KB of activation codes and 200 KB of weights at M = 64,
+  // K = N = 5120 (most of them L2 hits, shared by the n-block's m-groups on
+  // one XCD) instead of 327 KB of codes and 82 KB of weights for two
+  // n-tiles x 64 rows, and the loads it keeps in flight stay few; the CU's
+  // limit on outstanding L2 requests is what bounds this GEMM.  Measured at
+  // M = 64, K = N = 5120: 8.7 us, against 10.3 us for an LDS-slab kernel of
+  // two n-tiles x 64 rows with every load in flight at once and 10.9 us for
+  // the streaming kernel's two n-tiles x 64 rows.  The debug window runs the
+  // same kernel, instantiated with the partial-sum stores.
+  if (a.mode == kW4A8 && a.M > 16) {
     p.ms = (p.M + 15) / 16;
-    const dim3 grid((unsigned)(p.N / 16 / kMsplitNT * p.ms));
-    skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false><<<grid, dim3(512), 0, st>>>(p);
-    return hipGetLastError();
-  }
-  if (a.mode == kW4A8 && a.dbg == nullptr && a.M > 32 && p.G <= 8 * kDecodeGPW && p.N / 16 <= 1024) {
-    const dim3 grid((unsigned)((p.N / 16 + 1) / 2));
-    if (p.M > 48)
-      decode_w4a8_kernel<4, kDecodeGPW><<<grid, dim3(512), 0, st>>>(p);
+    p.wgs = (p.N / 16 + kMsplitNT - 1) / kMsplitNT;
+    const dim3 grid((unsigned)(p.wgs * p.ms));
+    if (a.dbg)
+      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, true><<<grid, dim3(512), 0, st>>>(p);
     else
-      decode_w4a8_kernel<3, kDecodeGPW><<<grid, dim3(512), 0, st>>>(p);
+      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false><<<grid, dim3(512), 0, st>>>(p);
     return hipGetLastError();
   }
   const SkinnyPlan pl = skinny_plan(a.mode, a.N, a.K);

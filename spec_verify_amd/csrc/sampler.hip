@@ -22,8 +22,9 @@
 // Pass 1: one workgroup of 256 threads per (row, chunk of 256*E logits),
 // the chunk held in registers.  Each wave's maximum and sum of
 // exp((x - max)/T) go to the workspace (shuffles only), and so do the
-// chunk's k largest keys in rank order.  Selection: every wave finds the k-th largest of its lanes' own
-// maxima with 40 ballots (at least k keys of the chunk reach it, so all of
+// chunk's k largest keys in rank order.  Selection: every wave finds the
+// k-th largest of its lanes' own maximum value codes (16 bits) with 16
+// ballots, one per bit (at least k keys of the chunk reach it, so all of
 // the chunk's top k do); the keys at or above the largest of those
 // thresholds, typically a few dozen, are compacted to LDS and ranked by
 // counting.  A radix select (8-bit digits, LDS histogram) takes over when

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(qg.lib, n), n
     assert set(names) == set(qg.EXPORTS)
@@ -207,3 +207,8 @@ def test_sampler_argument_errors():
     assert call_sampler(ws=MIS) == qg.QG_ERR_INVALID_ARG
     # no rows: nothing to do, no pointers needed
     assert call_sampler(R=0, x=None, u=None, out=None, ws=None, wsb=0) == qg.QG_OK
+
+
+def test_selftest_rejects_bad_counters():
+    assert qg.lib.qg_selftest_quant_division(None, None) == qg.QG_ERR_INVALID_ARG
+    assert qg.lib.qg_selftest_quant_division(ctypes.c_void_p((1 << 20) + 4), None) == qg.QG_ERR_INVALID_ARG

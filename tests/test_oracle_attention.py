@@ -6,10 +6,17 @@ reading is causal attention over the cache with grouped-query heads.  Pinned
 by a scalar evaluation of the definition on tiny inputs, closed forms and
 invariants (what a query may not see does not matter, heads of a group with
 equal queries agree, equal keys give the mean of the visible values).
+
+The score scale 1/sqrt(D) is a reading (the page gives head_dim 256 but not
+the scale); it is pinned by a closed form that does not restate the
+formula: with two visible keys whose dot products with the query differ by
+d, the two softmax weights stand in the ratio e^(d / sqrt(D)), read off an
+output whose value rows are unit vectors.  Planted scales (1/D, none) fail.
 """
 import math
 
 import numpy as np
+import pytest
 
 import oracle
 
@@ -69,3 +76,38 @@ def test_one_query_sees_everything_and_groups_share_values():
     k2[17, 0] = (q[0, 0].astype(np.float32) * 8).astype(np.float16)
     got2 = oracle.ref_verify_attention(q, k2, v)
     assert np.allclose(got2[0, 0], v[17, 0].astype(np.float64), atol=1e-6)
+
+
+def _two_key_weight_ratios(attn, D, scale_q=1.0):
+    """For (a, b) pairs: q = a e0 (times scale_q), keys 0 and b e0, values
+    e0 and e1.  The output's first two entries are the two softmax weights,
+    so out[1] / out[0] = exp((q . k1 - q . k0) * scale) = exp(a b * scale).
+    Returns [(ratio seen, a * b)]."""
+    out = []
+    for a, b in ((2.0, 4.0), (1.0, -8.0), (4.0, 8.0), (0.5, 3.0), (-2.0, 6.0)):
+        q = np.zeros((1, 1, D), np.float16)
+        q[0, 0, 0] = np.float16(a * scale_q)
+        k = np.zeros((2, 1, D), np.float16)
+        k[1, 0, 0] = b
+        v = np.zeros((2, 1, D), np.float16)
+        v[0, 0, 0] = 1.0
+        v[1, 0, 1] = 1.0
+        o = attn(q, k, v)
+        assert o[0, 0, 0] + o[0, 0, 1] == pytest.approx(1.0, abs=1e-15)
+        out.append((o[0, 0, 1] / o[0, 0, 0], a * b))
+    return out
+
+
+@pytest.mark.parametrize("D", [256, 64])
+def test_score_scale_closed_form(D):
+    for ratio, ab in _two_key_weight_ratios(oracle.ref_verify_attention, D):
+        assert ratio == pytest.approx(math.exp(ab / math.sqrt(D)), rel=1e-12), (D, ab)
+
+
+@pytest.mark.parametrize("planted,scale_q", [("1/D", 1.0 / 16.0), ("no scale", 16.0)])
+def test_planted_score_scales_fail_the_closed_form(planted, scale_q):
+    # q scaled by 1/16 (exact in fp16 for these values) is attention with
+    # scale 1/256 = 1/D at D = 256; q scaled by 16 is attention with no scale
+    got = _two_key_weight_ratios(oracle.ref_verify_attention, 256, scale_q)
+    assert all(q == pytest.approx(math.exp(ab * scale_q / 16.0), rel=1e-12) for q, ab in got)
+    assert not any(q == pytest.approx(math.exp(ab / 16.0), rel=1e-6) for q, ab in got), planted

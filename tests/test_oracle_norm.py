@@ -1,13 +1,16 @@
 """Pins for the oracle's RMSNorm and fused normalise-and-quantise step (CPU only).
 
 The pages name no norm, so ``oracle.rmsnorm`` is a reading (its docstring has
-the definition): parity unpinned as to the pages.  These tests pin the oracle
-to that definition by other means: an exact-rational evaluation of every
-rounding on small rows, closed forms, an exact invariance under power-of-two
-scaling, padding invariance of the tree sum, and a float64 bound.
+the definition: the float64 value of x * w / sqrt(mean(x^2) + eps), rounded
+once to fp16): parity unpinned as to the pages.  These tests pin the oracle
+to that definition by other means: a 60-digit decimal evaluation rounded to
+fp16 by hand, closed forms (constant rows, with and without eps), exact
+invariances (power-of-two scaling of x without eps, the sign of x, doubling
+the weight), and planted mistakes in the norm (mean over H - 1, a dropped
+eps, a dropped square root) that the closed forms reject.
 """
+from decimal import Decimal, getcontext
 from fractions import Fraction
-import math
 
 import numpy as np
 import pytest
@@ -17,104 +20,91 @@ import synth
 from tests import exact
 
 
-def _ulp32(f: Fraction) -> Fraction:
-    a = abs(f)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    while Fraction(2) ** e > a:
-        e -= 1
-    while Fraction(2) ** (e + 1) <= a:
-        e += 1
-    return Fraction(2) ** (max(e, -126) - 23)
+def _decimal_norm_row(x, w, eps):
+    """fp16 values (as Fractions) of one row by 60-digit decimal arithmetic:
+    y = fp16(x * w / sqrt(sum(x^2) / H + eps)), rounded by hand."""
+    getcontext().prec = 60
+    xs = [Decimal(float(v)) for v in x]                      # fp16 -> float -> Decimal: exact
+    ws = [Decimal(float(v)) for v in w]
+    H = len(xs)
+    t = sum(v * v for v in xs) / H + Decimal(float(np.float32(eps)))
+    if t == 0:
+        return [Fraction(0)] * H
+    r = 1 / t.sqrt()
+    return [exact.round_f16(Fraction(v * r * wv)) for v, wv in zip(xs, ws)]
 
 
-def _rn_sqrt32(t: Fraction) -> Fraction:
-    """Correctly rounded float32 square root of t, checked exactly: the
-    candidate's half-ulp neighbourhood must contain sqrt(t)."""
-    f = Fraction(float(np.sqrt(np.float32(float(t)))))
-    for cand in (f, f + _ulp32(f), f - _ulp32(f)):
-        half_lo = _ulp32(cand - _ulp32(cand) / 4) / 2 if cand > 0 else Fraction(0)
-        half_hi = _ulp32(cand) / 2
-        if (cand - half_lo) ** 2 <= t <= (cand + half_hi) ** 2:
-            return cand
-    raise AssertionError("no correctly rounded square root found")
+def _as_fractions(y):
+    return [Fraction(float(v)) for v in y]
 
 
-def _exact_factor(x, eps):
-    """r of the definition for one row, with exact rationals, rounding by hand."""
-    H = len(x)
-    sq = [Fraction(float(v)) ** 2 for v in x]
-    assert all(exact.round_f32(s) == s for s in sq)        # squares are exact in fp32
-    p = 1
-    while p < H:
-        p *= 2
-    level = sq + [Fraction(0)] * (p - H)
-    while len(level) > 1:
-        level = [exact.round_f32(level[i] + level[i + 1]) for i in range(0, len(level), 2)]
-    t = exact.round_f32(exact.round_f32(level[0] / H) + Fraction(float(np.float32(eps))))
-    return exact.round_f32(1 / _rn_sqrt32(t)) if t > 0 else Fraction(0)
-
-
-@pytest.mark.parametrize("H,eps", [(5, 1e-6), (8, 0.25), (13, 3e-3), (16, 0.0)])
-def test_rmsnorm_factor_matches_an_exact_evaluation(H, eps):
-    rng = np.random.default_rng(H)
-    mags = np.exp(rng.uniform(np.log(1e-3), np.log(30.0), size=(1500, 1)))
-    x = (rng.standard_normal((1500, H)) * mags).astype(np.float16)
-    r = oracle.rmsnorm_factor(x, eps)
-    for m in range(len(x)):
-        assert Fraction(float(r[m])) == _exact_factor(x[m], eps), (H, eps, m)
-
-
-@pytest.mark.parametrize("H,seed", [(5, 1), (8, 2), (13, 3), (128, 4)])
-def test_rmsnorm_products_match_an_exact_evaluation(H, seed):
+@pytest.mark.parametrize("H,eps,seed", [(5, 1e-6, 1), (8, 0.25, 2), (13, 3e-3, 3), (128, 0.0, 4), (640, 1e-5, 5)])
+def test_matches_a_decimal_evaluation(H, eps, seed):
     rng = np.random.default_rng(seed)
-    x = (rng.standard_normal((3, H)) * np.array([[0.01], [1.0], [300.0]])).astype(np.float16)
+    rows = 400 if H <= 128 else 40
+    mags = np.exp(rng.uniform(np.log(1e-3), np.log(30.0), size=(rows, 1)))
+    x = (rng.standard_normal((rows, H)) * mags).astype(np.float16)
     w = (1.0 + 0.5 * rng.standard_normal(H)).astype(np.float16)
-    for eps in (1e-6, 0.25):
-        y32 = oracle.rmsnorm_f32(x, w, eps)
-        y16 = oracle.rmsnorm(x, w, eps)
-        for m in range(3):
-            r = _exact_factor(x[m], eps)
-            want = [exact.round_f32(exact.round_f32(Fraction(float(v)) * r) * Fraction(float(wv)))
-                    for v, wv in zip(x[m], w)]
-            assert [Fraction(float(v)) for v in y32[m]] == want, (H, m, eps)
-            assert [Fraction(float(v)) for v in y16[m]] == [exact.round_f16(v) for v in want]
+    y = oracle.rmsnorm(x, w, eps)
+    for m in range(rows):
+        assert _as_fractions(y[m]) == _decimal_norm_row(x[m], w, eps), (H, eps, m)
 
 
-def test_tree_sum_closed_form_and_padding():
-    v = np.array([[1e8, 1.0, -1e8, 1.0, 3.0]], np.float32)
-    # ((v0 + v1) + (v2 + v3)) + (v4 + 0): fp32(1e8 + 1) = 1e8, so the 1s vanish
-    a = np.float32(np.float32(1e8) + np.float32(1.0))
-    b = np.float32(np.float32(-1e8) + np.float32(1.0))
-    want = np.float32(np.float32(a + b) + np.float32(3.0))
-    assert oracle.tree_sum_f32(v)[0] == want == np.float32(3.0)
-    rng = np.random.default_rng(7)
-    w = rng.standard_normal((4, 37)).astype(np.float32)
-    padded = np.concatenate([w, np.zeros((4, 91), np.float32)], axis=1)
-    assert np.array_equal(oracle.tree_sum_f32(w), oracle.tree_sum_f32(padded))
-    ints = rng.integers(-1000, 1000, size=(3, 640)).astype(np.float32)     # every partial sum exact
-    assert np.array_equal(oracle.tree_sum_f32(ints), ints.sum(axis=1))
+def test_decimal_evaluation_on_workload_rows():
+    x = synth.acts(3, 5120, 1.0, 0.01, 20.0, seed=11)
+    w = (1.0 + 0.1 * synth.acts(1, 5120, 1.0, 0.0, 1.0, seed=12)[0].astype(np.float32)).astype(np.float16)
+    y = oracle.rmsnorm(x, w, 1e-6)
+    for m in range(3):
+        assert _as_fractions(y[m]) == _decimal_norm_row(x[m], w, 1e-6), m
 
 
-def test_tree_sum_error_bound_against_exact_sum():
-    rng = np.random.default_rng(8)
-    v = (rng.standard_normal((6, 5120)) ** 2).astype(np.float32)
-    got = oracle.tree_sum_f32(v)
-    for m in range(6):
-        ex = math.fsum(float(t) for t in v[m])
-        bound = math.ceil(math.log2(5120)) * 2.0 ** -24 * math.fsum(abs(float(t)) for t in v[m])
-        assert abs(float(got[m]) - ex) <= bound
+def _planted(kind):
+    """Norms with one planted mistake each, for the closed-form pins to reject."""
+    def f(x, w, eps):
+        xf = x.astype(np.float64)
+        H = xf.shape[1]
+        ss = (xf * xf).sum(axis=1, keepdims=True)
+        if kind == "mean over H-1":
+            t = ss / (H - 1) + eps
+        elif kind == "no eps":
+            t = ss / H
+        elif kind == "no sqrt":
+            return (xf / (ss / H + eps) * w.astype(np.float64)).astype(np.float16)
+        return (xf / np.sqrt(t) * w.astype(np.float64)).astype(np.float16)
+    return f
 
 
-def test_constant_rows_normalise_to_the_weight():
+def _constant_row_pins(norm):
+    """Closed forms: a constant row c gives r = 1 / sqrt(c^2 + eps), so
+    y = w * sign(c) at eps = 0 and fp16(w * c / sqrt(c^2 + eps)) otherwise."""
     H = 256
     x = np.zeros((3, H), np.float16)
     x[0] = np.float16(4.0)
     x[1] = np.float16(-0.125)
+    x[2] = np.float16(1.0)
     w = np.full(H, np.float16(1.5))
-    y = oracle.rmsnorm(x, w, 0.0)
-    assert (y[0] == np.float16(1.5)).all() and (y[1] == np.float16(-1.5)).all()
-    assert not y[2].any()                                    # zero row, eps = 0: r = 0
-    assert not oracle.rmsnorm(x[2:], w, 1e-6).any()
+    y0 = norm(x, w, 0.0)
+    ok = bool((y0[0] == np.float16(1.5)).all() and (y0[1] == np.float16(-1.5)).all())
+    # c = 1, eps = 0.25: y = 1.5 / sqrt(1.25) = 1.5 * 2 / sqrt(5) = 3 / sqrt(5)
+    getcontext().prec = 60
+    want = exact.round_f16(Fraction(Decimal(3) / Decimal(5).sqrt()))
+    ye = norm(x, w, 0.25)
+    ok = ok and all(Fraction(float(v)) == want for v in ye[2])
+    return ok
+
+
+def test_constant_rows_normalise_to_the_weight():
+    assert _constant_row_pins(oracle.rmsnorm)
+    H = 256
+    z = np.zeros((2, H), np.float16)
+    w = np.full(H, np.float16(1.5))
+    assert not oracle.rmsnorm(z, w, 0.0).astype(np.float32).any()   # zero row, eps = 0: r = 0
+    assert not oracle.rmsnorm(z, w, 1e-6).astype(np.float32).any()
+
+
+@pytest.mark.parametrize("kind", ["mean over H-1", "no eps", "no sqrt"])
+def test_planted_mistakes_fail_the_closed_forms(kind):
+    assert not _constant_row_pins(_planted(kind))
 
 
 def test_power_of_two_scaling_is_exact_without_eps():
@@ -129,14 +119,15 @@ def test_power_of_two_scaling_is_exact_without_eps():
         assert np.array_equal(oracle.rmsnorm(xs, w, 0.0).view(np.uint16), y.view(np.uint16)), k
 
 
-def test_rmsnorm_within_one_fp16_ulp_of_float64():
-    x = synth.acts(16, 5120, 1.0, 0.01, 20.0, seed=11)
-    w = (1.0 + 0.1 * synth.acts(1, 5120, 1.0, 0.0, 1.0, seed=12)[0].astype(np.float32)).astype(np.float16)
-    y = oracle.rmsnorm(x, w, 1e-6).astype(np.float64)
-    xf = x.astype(np.float64)
-    y64 = xf / np.sqrt((xf * xf).mean(axis=1, keepdims=True) + 1e-6) * w.astype(np.float64)[None, :]
-    ulp = np.spacing(np.abs(y64).astype(np.float16)).astype(np.float64)
-    assert (np.abs(y - y64) <= ulp * 1.01).all()
+def test_sign_and_weight_doubling_are_exact():
+    x = synth.acts(6, 384, 1.0, 0.01, 20.0, seed=15)
+    w = synth.acts(1, 384, 0.5, 0.0, 1.0, seed=16)[0]
+    y = oracle.rmsnorm(x, w, 1e-5).astype(np.float32)
+    assert np.array_equal(oracle.rmsnorm(-x, w, 1e-5).astype(np.float32), -y)
+    w2 = (w.astype(np.float32) * 2).astype(np.float16)
+    y2 = oracle.rmsnorm(x, w2, 1e-5).astype(np.float32)
+    normal = np.abs(y) >= 2.0 ** -14                         # doubling is exact outside the subnormals
+    assert normal.mean() > 0.9 and np.array_equal(y2[normal], 2 * y[normal])
 
 
 def test_fused_step_is_the_quantiser_on_the_normalised_rows():
