@@ -290,6 +290,30 @@ int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H,
                      int8_t* Q, void* S_f16, void* stream);
 
 /*
+ * w4a8_gemm_noalloc -- w4a8_gemm for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results as w4a8_gemm (bit-identical y), minus the workspace: the int8
+ * activation codes and token scales go to a device array inside the
+ * library, QG_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held from the first
+ * call on that GPU until the process ends.  Nothing is allocated and the
+ * host is not synchronised (the first call on a GPU looks up the array's
+ * device address once).
+ *   Requires w4a8_prepared_bytes(M, K) <= QG_NOALLOC_SCRATCH_BYTES (any
+ *   M <= 64 with K <= 130,944; M = 4096 with K <= 1,920); a larger shape
+ *   returns QG_ERR_WORKSPACE before anything runs.
+ *   The array needs no initialisation and keeps the last call's codes.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on
+ *   one GPU (on different streams, or from several threads without an
+ *   ordering between their streams) race and give undefined results.
+ * w4a8_noalloc_scratch_bytes() returns QG_NOALLOC_SCRATCH_BYTES.
+ */
+#define QG_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+size_t w4a8_noalloc_scratch_bytes(void);
+int w4a8_gemm_noalloc(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
+                      const void* w_packed, const void* s_packed, void* y_f16, void* stream);
+
+/*
  * qg_selftest_quant_division -- exhaustive device check of the quantiser's
  * division ([OPT] "In full" item 4: per-token int8 activations; codes are
  * rint(x / scale) with scale = absmax / 127).  The kernels form x / scale as

@@ -66,6 +66,8 @@ _SIGS = {
     "embed_gather_dequant_int8": (ctypes.c_int, [_p, _i64, _p, _p, _i64, _i64, _p, _p]),
     "quant_table_int8": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
     "qg_selftest_quant_division": (ctypes.c_int, [_p, _p]),
+    "w4a8_noalloc_scratch_bytes": (_sz, []),
+    "w4a8_gemm_noalloc": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -173,6 +175,16 @@ def w4a8_gemm(x, w_packed, s_packed, N, y=None, workspace=None):
     ws, wsz = _workspace(QG_OP_W4A8, M, K, N, x, workspace)
     _check("w4a8_gemm", lib.w4a8_gemm(_ptr(x), M, K, N, _ldx(x), _ptr(w_packed), _ptr(s_packed), _ptr(y),
                                       _ptr(ws), wsz, _stream(x.device)))
+    return y
+
+
+def w4a8_gemm_noalloc(x, w_packed, s_packed, N, y):
+    """y = the W4A8 product of fp16 x [M, K] with packed weights, through the
+    entry point that takes no workspace (its scratch is a device array inside
+    the library).  The caller passes y (fp16 [M, N]); nothing is allocated."""
+    M, K = x.shape
+    _check("w4a8_gemm_noalloc", lib.w4a8_gemm_noalloc(_ptr(x), M, K, N, _ldx(x), _ptr(w_packed), _ptr(s_packed),
+                                                      _ptr(y), _stream(x.device)))
     return y
 
 

@@ -1,7 +1,9 @@
 // C-ABI entry points of libqgemm: host-side validation, workspace layout and
 // dispatch to the gfx950 kernels.  Nothing here allocates device memory or
 // synchronises the host; every check happens before the first launch.
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include "qgemm.h"
 
 #include <stdint.h>
@@ -392,6 +394,86 @@ int w4a8_gemm_prepared(const void* prepared, int64_t M, int64_t K, int64_t N, co
   if (M == 0) return QG_OK;
   clear_stale_error();
   return gemm_prepared_impl(prepared, M, K, N, w_packed, s_packed, y_f16, as_stream(stream), nullptr, 0, 0, 0, 0);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// w4a8_gemm without a caller workspace (w4a8_gemm_noalloc).  The int8 codes
+// and token scales that w4a8_gemm keeps in its workspace live here in a
+// file-scope device array, `scratch`; each GPU holds its own copy, at its
+// own address, for the life of the process.  Host code never passes the
+// array's name to a kernel (in host code it names a host-side stand-in, not
+// device memory): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[QG_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_addr[kMaxDevices];   // device address of scratch per device, null until looked up
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the device that runs `stream` (looked up
+// on the first call for that device), or null with *err set.
+void* scratch_for_stream(hipStream_t stream, hipError_t* err) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* addr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (addr) return addr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  addr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (addr) return addr;
+  int cur = -1;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (cur != dev) {
+    const hipError_t back = hipSetDevice(cur);
+    if (e == hipSuccess) e = back;
+  }
+  if (e != hipSuccess || addr == nullptr) {
+    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  g_scratch_addr[dev].store(addr, std::memory_order_release);
+  return addr;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t w4a8_noalloc_scratch_bytes(void) { return QG_NOALLOC_SCRATCH_BYTES; }
+
+int w4a8_gemm_noalloc(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const void* w_packed,
+                      const void* s_packed, void* y_f16, void* stream) {
+  int st = check_gemm_shape(M, K, N, ldx);
+  if (st != QG_OK) return st;
+  if ((st = check_ptrs(M, x_f16, w_packed, s_packed, y_f16)) != QG_OK) return st;
+  if (M == 0) return QG_OK;
+  const size_t need = w4a8_layout(M, K).total;
+  if (need > QG_NOALLOC_SCRATCH_BYTES) return QG_ERR_WORKSPACE;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_for_stream(as_stream(stream), &e);
+  if (ws == nullptr) return launch_status(e);
+  return w4a8_impl(x_f16, M, K, N, ldx, w_packed, s_packed, y_f16, ws, need, stream, nullptr, nullptr, nullptr, 0, 0,
+                   0, 0);
 }
 
 int w8a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx, const int8_t* w,

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(qg.lib, n), n
     assert set(names) == set(qg.EXPORTS)
@@ -212,3 +212,16 @@ def test_sampler_argument_errors():
 def test_selftest_rejects_bad_counters():
     assert qg.lib.qg_selftest_quant_division(None, None) == qg.QG_ERR_INVALID_ARG
     assert qg.lib.qg_selftest_quant_division(ctypes.c_void_p((1 << 20) + 4), None) == qg.QG_ERR_INVALID_ARG
+
+
+def test_noalloc_gemm_rejects_shapes_beyond_its_scratch():
+    limit = qg.lib.w4a8_noalloc_scratch_bytes()
+    assert limit == 8 << 20
+    assert qg.lib.w4a8_prepared_bytes(64, 130944) <= limit < qg.lib.w4a8_prepared_bytes(64, 131072)
+    f = qg.lib.w4a8_gemm_noalloc
+    assert f(FAKE, 64, 131072, 16, 131072, FAKE, FAKE, FAKE, None) == qg.QG_ERR_WORKSPACE
+    assert f(FAKE, 4096, 2048, 16, 2048, FAKE, FAKE, FAKE, None) == qg.QG_ERR_WORKSPACE
+    assert f(FAKE, 0, 256, 16, 256, FAKE, FAKE, FAKE, None) == qg.QG_OK
+    assert f(FAKE, 4, 200, 16, 200, FAKE, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert f(MIS, 4, 256, 16, 256, FAKE, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+    assert f(None, 4, 256, 16, 256, FAKE, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
