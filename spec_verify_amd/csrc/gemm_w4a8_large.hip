@@ -21,17 +21,25 @@
 // part fall in 16 distinct groups of 4 banks.
 //
 // Rescale.  Per group and tile two v_mfma_i32_16x16x64_i8 give 16 * P
-// exactly; acc += fp32(16 P) * s (fp16 scale operand of v_fma_mix), and the
-// factor 1/16 joins the token scale in the epilogue.  That is two VALU
-// operations per output element per group, about as much issue time as the
-// matrix-core work itself.  The kernel is sized for three workgroups per CU
-// (at most 168 VGPRs, 48.5 KiB of LDS), so three waves share each SIMD and
-// one wave's rescale runs beside another's matrix-core work.
+// exactly, started from the bits of C = 1.5 * 2^23 so that the int32 result
+// read as fp32 is C + 16 P; then acc += (C + 16 P) * s (fp16 scale operand
+// of v_fma_mix) with no int-to-float conversion, and the bias C * s is
+// taken off every four groups (below).  The factor 1/16 joins the token
+// scale in the epilogue.  That is one vector FMA per output element and
+// group plus a quarter for the bias: vector and matrix-core work still take
+// turns on a SIMD more than they overlap (counters: the matrix core busy
+// 43% of the cycles, other vector instructions 55%, both at once 15%), so
+// every vector instruction per group costs time.  The kernel is sized for
+// three workgroups per CU (at most 168 VGPRs, 48.5 KiB of LDS), so three
+// waves share each SIMD and one wave's rescale runs beside another's
+// matrix-core work.
 //
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin; ids are
 // remapped so each XCD walks a contiguous run of a grouped tile order (8
 // m-blocks by the n-blocks), and the workgroups resident together on an XCD
 // share activation and weight slices in its L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace qg {
@@ -39,6 +47,20 @@ namespace {
 
 constexpr int BM = 128, BN = 128, GROUP_M = 8;
 constexpr uint32_t kHiNib = 0xF0F0F0F0u;
+
+// Conversion-free rescale.  Each group's first MFMA starts from the int32
+// bits of C = 1.5 * 2^23 instead of zero, so the group's result, read as
+// fp32, is exactly C + 16 P (|16 P| <= 16 * 127 * 8 * 128 < 2^22 keeps it
+// in C's binade, where consecutive integers are consecutive floats).  Then
+// acc += (C + 16 P) * s needs no int-to-float conversion; the bias C * s is
+// summed per column and taken off every kBiasGroups groups, before it grows
+// large enough to cost the accumulator precision.  On the prefill workload
+// the fp16 outputs' relative Frobenius error against the float64 reference
+// is 2.5e-4 (2.1e-4 with a conversion per group; 2.9e-4 with the bias taken
+// off every 8 groups; the bound is 5e-4).
+constexpr int32_t kBiasBits = 0x4B400000;
+constexpr float kBias = 12582912.0f;
+constexpr int kBiasGroups = 4;
 
 struct LargeParams {
   const int8_t* codes;
@@ -53,6 +75,16 @@ struct LargeParams {
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// lo += fp32(low half of h), hi += fp32(high half of h), h two fp16: one
+// mixed-precision FMA each (x * 1.0 + acc with x read as fp16), where the
+// compiler would otherwise convert and add in two instructions.
+__device__ __forceinline__ void add_f16_pair(float& lo, float& hi, uint32_t h) {
+  asm("v_fma_mix_f32 %0, %2, 1.0, %0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %1, %2, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(lo), "+v"(hi)
+      : "v"(h));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -128,6 +160,11 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[j][mt] = (f32x4)0.0f;
+  float ssum[4][4];   // this lane's columns: sum of the group scales since the last bias correction
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ssum[j][r] = 0.0f;
 
   // LDS byte offsets of this lane's activation operands: m-tile mt, half h
   // (k 64h + 16 quad .. +15 of the group = part 4h + quad).
@@ -143,8 +180,11 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
+  // One group g whose operands sit in stage BUF (a constant: the loop runs
+  // two groups per iteration, so the LDS addresses of both stages are fixed
+  // offsets and cost no vector instructions).
+  auto group = [&](int g, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
     // All of this group's operands come out of LDS first; only then are the
     // next group's LDS-direct loads issued (into the other stage), so no
     // LDS read of this group waits behind them.
@@ -174,12 +214,18 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
                               __builtin_bit_cast(_Float16, (uint16_t)(sv[j].x >> 16)),
                               __builtin_bit_cast(_Float16, (uint16_t)(sv[j].y & 0xFFFFu)),
                               __builtin_bit_cast(_Float16, (uint16_t)(sv[j].y >> 16))};
+      add_f16_pair(ssum[j][0], ssum[j][1], sv[j].x);
+      add_f16_pair(ssum[j][2], ssum[j][3], sv[j].y);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xb[mt][0], (i32x4)0, 0, 0, 0);
+        i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xb[mt][0], (i32x4)kBiasBits, 0, 0, 0);
         P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, xb[mt][1], P, 0, 0, 0);
+        // The whole vector is reinterpreted at once: taking element r of the
+        // int vector and then its bits as float made the compiler feed
+        // element 0 to all four mixed-precision FMAs.
+        const f32x4 F = __builtin_bit_cast(f32x4, P);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf((float)P[r], (float)s4[r], acc[j][mt][r]);
+        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(F[r], (float)s4[r], acc[j][mt][r]);
         if constexpr (DEBUG) {
           const int m = m0 + wm * 64 + mt * 16 + col;
           if (m >= p.dm0 && m < p.dm1 && m < p.M) {
@@ -187,17 +233,34 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
             for (int r = 0; r < 4; ++r) {
               const int n = (nt_base + wn * 4 + j) * 16 + 4 * quad + r;
               if (n >= p.dn0 && n < p.dn1 && n < p.N)
-                p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * G + g] = P[r] >> 4;
+                p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * G + g] = (P[r] - kBiasBits) >> 4;
             }
           }
         }
+      }
+    }
+    if ((g % kBiasGroups) == kBiasGroups - 1 || g == G - 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(-kBias, ssum[j][r], acc[j][mt][r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ssum[j][r] = 0.0f;
       }
     }
     // This wave's loads for group g + 1 have landed; after the barrier,
     // every wave's have, and nobody reads this stage any more.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  int g = 0;
+  for (; g + 2 <= G; g += 2) {
+    group(g, std::integral_constant<int, 0>{});
+    group(g + 1, std::integral_constant<int, 1>{});
   }
+  if (g < G) group(g, std::integral_constant<int, 0>{});
 
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
