@@ -26,13 +26,13 @@
 // of v_fma_mix) with no int-to-float conversion, and the bias C * s is
 // taken off every four groups (below).  The factor 1/16 joins the token
 // scale in the epilogue.  That is one vector FMA per output element and
-// group plus a quarter for the bias: vector and matrix-core work still take
-// turns on a SIMD more than they overlap (counters: the matrix core busy
-// 43% of the cycles, other vector instructions 55%, both at once 15%), so
-// every vector instruction per group costs time.  The kernel is sized for
-// three workgroups per CU (at most 168 VGPRs, 48.5 KiB of LDS), so three
-// waves share each SIMD and one wave's rescale runs beside another's
-// matrix-core work.
+// group plus a quarter for the bias; one wave sums the window's scales for
+// the whole workgroup and shares them through LDS.  Within a group the
+// tiles are software-pipelined (each tile's products go out around the
+// previous tile's rescale).  The kernel is sized for three workgroups per
+// CU (at most 168 VGPRs, 49 KiB of LDS).  Under this load the part runs
+// at its power limit (about 2.0-2.2 GHz), so every instruction and byte
+// moved per group costs time.
 //
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin; ids are
 // remapped so each XCD walks a contiguous run of a grouped tile order (8
@@ -104,6 +104,10 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
   __shared__ __attribute__((aligned(16))) int8_t As[2][BM * 128];
   __shared__ __attribute__((aligned(16))) uint4 Bs[2][8 * 64];
   __shared__ __attribute__((aligned(16))) uint32_t Ss[2][64];   // 128 fp16 scales: [n-tile][16]
+  // Per column: the scale sum of a bias window (below), alternating between
+  // two buffers so that a window ending one group after another cannot
+  // overwrite sums that other waves are still reading.
+  __shared__ __attribute__((aligned(16))) float WS[2][128];
 
   // Tile of this workgroup (see "Placement").
   const int xcd = blockIdx.x & 7;
@@ -134,24 +138,27 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
   // Per-lane offsets of the staging loads (the group adds a scalar offset).
   // A: wave w loads 1 KiB chunks c = 4w .. 4w+3 (rows 8c .. 8c+7); lane l
   // fills row 8c + l/8, slot l%8 with part (l%8) ^ ((row/2) % 8).
-  uint32_t va[4];
+  // Chunks i and i + 2 are 16 rows apart, which leaves the swizzle
+  // unchanged: they share a lane offset and differ by a scalar 16 K.
+  uint32_t va[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int r = 8 * (4 * wave + i) + (lane >> 3);
     va[i] = (uint32_t)r * (uint32_t)p.K + 16u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7));
   }
-  // B: wave w loads n-tiles 2w, 2w+1 (one 1 KiB block each).
-  uint32_t vb[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) vb[i] = ((uint32_t)(2 * wave + i) * (uint32_t)G * 64u + lane) * 16u;
+  const uint32_t a_step = 16u * (uint32_t)p.K;
+  // B: wave w loads n-tiles 2w, 2w+1 (one 1 KiB block each, G KiB apart).
+  const uint32_t vb = ((uint32_t)(2 * wave) * (uint32_t)G * 64u + lane) * 16u;
+  const uint32_t b_step = (uint32_t)G * 1024u;
   // S (wave 0): lane l loads scales 2(l%8), +1 of n-tile l/8.
   const uint32_t vs = (((uint32_t)(lane >> 3) * (uint32_t)G) * 16u + 2u * (lane & 7)) * 2u;
 
   auto gload = [&](int g, int8_t* A, uint4* B, uint32_t* S) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ld_lds16(rsA, A + (4 * wave + i) * 1024, va[i], (uint32_t)g * 128u);
+    for (int i = 0; i < 4; ++i)
+      ld_lds16(rsA, A + (4 * wave + i) * 1024, va[i & 1], (uint32_t)g * 128u + (uint32_t)(i >> 1) * a_step);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ld_lds16(rsB, B + (2 * wave + i) * 64, vb[i], (uint32_t)g * 1024u);
+    for (int i = 0; i < 2; ++i) ld_lds16(rsB, B + (2 * wave + i) * 64, vb, (uint32_t)g * 1024u + (uint32_t)i * b_step);
     if (wave == 0) ld_lds4(rsS, S, vs, (uint32_t)g * 32u);
   };
 
@@ -160,11 +167,9 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[j][mt] = (f32x4)0.0f;
-  float ssum[4][4];   // this lane's columns: sum of the group scales since the last bias correction
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ssum[j][r] = 0.0f;
+  // Wave 0 sums each window's scales for the whole workgroup, two columns
+  // per lane (word `lane` of a scale stage: columns 2 lane, 2 lane + 1).
+  float ws0 = 0.0f, ws1 = 0.0f;
 
   // LDS byte offsets of this lane's activation operands: m-tile mt, half h
   // (k 64h + 16 quad .. +15 of the group = part 4h + quad).
@@ -200,60 +205,103 @@ __global__ __launch_bounds__(256, 3) void w4a8_large_kernel(LargeParams p) {
       wv[j] = Bs[buf][(wn * 4 + j) * 64 + lane];
       sv[j] = *reinterpret_cast<const uint2*>(&Ss[buf][(wn * 4 + j) * 8 + 2 * quad]);
     }
+    const bool window_end = (g % kBiasGroups) == kBiasGroups - 1 || g == G - 1;
+    float* const wsum_buf = WS[(g / kBiasGroups) & 1];
+    if (wave == 0) {
+      add_f16_pair(ws0, ws1, Ss[buf][lane]);
+      if (window_end) {
+        *reinterpret_cast<float2*>(&wsum_buf[2 * lane]) = float2{ws0, ws1};
+        ws0 = 0.0f;
+        ws1 = 0.0f;
+      }
+    }
     if (g + 1 < G) gload(g + 1, As[buf ^ 1], Bs[buf ^ 1], Ss[buf ^ 1]);
 
+    // Software pipeline over the 16 tiles t = (n-tile j, m-tile mt): tile
+    // t's two matrix-core products go out around tile t - 1's rescale and a
+    // quarter of the next n-tile's unpack, so that vector work issues while
+    // the matrix core runs instead of waiting for the product it reads.
+    // Scheduling barriers hold that order; the empty asm on each rescaled
+    // accumulator keeps the compiler from sinking the rescales to the end
+    // of the group (where all 16 products would be live at once).
+    auto unpack_half = [&](uint32_t w, i32x4& a, int k) {
+      a[2 * k] = (int32_t)((w << 4) & kHiNib);
+      a[2 * k + 1] = (int32_t)(w & kHiNib);
+    };
+    auto scale = [&](int j, int r) -> float {
+      const uint32_t h = (r < 2) ? sv[j].x : sv[j].y;
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? (h >> 16) : (h & 0xFFFFu)));
+    };
+    i32x4 wa[2][2];   // unpacked int8 operands (16 q) of n-tiles j and j + 1
+    unpack_half(wv[0].x, wa[0][0], 0);
+    unpack_half(wv[0].y, wa[0][0], 1);
+    unpack_half(wv[0].z, wa[0][1], 0);
+    unpack_half(wv[0].w, wa[0][1], 1);
+    i32x4 Pp;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 w = wv[j];
-      i32x4 a0, a1;
-      a0[0] = (int32_t)((w.x << 4) & kHiNib); a0[1] = (int32_t)(w.x & kHiNib);
-      a0[2] = (int32_t)((w.y << 4) & kHiNib); a0[3] = (int32_t)(w.y & kHiNib);
-      a1[0] = (int32_t)((w.z << 4) & kHiNib); a1[1] = (int32_t)(w.z & kHiNib);
-      a1[2] = (int32_t)((w.w << 4) & kHiNib); a1[3] = (int32_t)(w.w & kHiNib);
-      const _Float16 s4[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sv[j].x & 0xFFFFu)),
-                              __builtin_bit_cast(_Float16, (uint16_t)(sv[j].x >> 16)),
-                              __builtin_bit_cast(_Float16, (uint16_t)(sv[j].y & 0xFFFFu)),
-                              __builtin_bit_cast(_Float16, (uint16_t)(sv[j].y >> 16))};
-      add_f16_pair(ssum[j][0], ssum[j][1], sv[j].x);
-      add_f16_pair(ssum[j][2], ssum[j][3], sv[j].y);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, xb[mt][0], (i32x4)kBiasBits, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, xb[mt][1], P, 0, 0, 0);
+    for (int t = 0; t < 16; ++t) {
+      const int j = t >> 2, mt = t & 3;
+      const int jp = (t - 1) >> 2, mp = (t - 1) & 3;
+      __builtin_amdgcn_sched_barrier(0);
+      i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[j & 1][0], xb[mt][0], (i32x4)kBiasBits, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t > 0) {
         // The whole vector is reinterpreted at once: taking element r of the
         // int vector and then its bits as float made the compiler feed
         // element 0 to all four mixed-precision FMAs.
-        const f32x4 F = __builtin_bit_cast(f32x4, P);
+        const f32x4 F = __builtin_bit_cast(f32x4, Pp);
+        acc[jp][mp][0] = __builtin_fmaf(F[0], scale(jp, 0), acc[jp][mp][0]);
+        acc[jp][mp][1] = __builtin_fmaf(F[1], scale(jp, 1), acc[jp][mp][1]);
+        asm volatile("" : "+v"(acc[jp][mp]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      P = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[j & 1][1], xb[mt][1], P, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t > 0) {
+        const f32x4 F = __builtin_bit_cast(f32x4, Pp);
+        acc[jp][mp][2] = __builtin_fmaf(F[2], scale(jp, 2), acc[jp][mp][2]);
+        acc[jp][mp][3] = __builtin_fmaf(F[3], scale(jp, 3), acc[jp][mp][3]);
+        asm volatile("" : "+v"(acc[jp][mp]));
+      }
+      if (j < 3) {
+        const uint32_t w = mt == 0 ? wv[j + 1].x : mt == 1 ? wv[j + 1].y : mt == 2 ? wv[j + 1].z : wv[j + 1].w;
+        unpack_half(w, wa[(j + 1) & 1][mt >> 1], mt & 1);
+      }
+      if constexpr (DEBUG) {
+        const int m = m0 + wm * 64 + mt * 16 + col;
+        if (m >= p.dm0 && m < p.dm1 && m < p.M) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(F[r], (float)s4[r], acc[j][mt][r]);
-        if constexpr (DEBUG) {
-          const int m = m0 + wm * 64 + mt * 16 + col;
-          if (m >= p.dm0 && m < p.dm1 && m < p.M) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int n = (nt_base + wn * 4 + j) * 16 + 4 * quad + r;
-              if (n >= p.dn0 && n < p.dn1 && n < p.N)
-                p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * G + g] = (P[r] - kBiasBits) >> 4;
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int n = (nt_base + wn * 4 + j) * 16 + 4 * quad + r;
+            if (n >= p.dn0 && n < p.dn1 && n < p.N)
+              p.dbg[((int64_t)(m - p.dm0) * (p.dn1 - p.dn0) + (n - p.dn0)) * G + g] = (P[r] - kBiasBits) >> 4;
           }
         }
       }
+      Pp = P;
     }
-    if ((g % kBiasGroups) == kBiasGroups - 1 || g == G - 1) {
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const f32x4 F = __builtin_bit_cast(f32x4, Pp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[3][3][r] = __builtin_fmaf(F[r], scale(3, r), acc[3][3][r]);
+    }
+    // This wave's loads for group g + 1 have landed; after the barrier,
+    // every wave's have, nobody reads this stage any more, and a window that
+    // ended here has its sums in LDS.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Take off the window's bias: C times each column's scale sum.
+    if (window_end) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const f32x4 wsum = *reinterpret_cast<const f32x4*>(&wsum_buf[(wn * 4 + j) * 16 + 4 * quad]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(-kBias, ssum[j][r], acc[j][mt][r]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ssum[j][r] = 0.0f;
+          for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(-kBias, wsum[r], acc[j][mt][r]);
       }
     }
-    // This wave's loads for group g + 1 have landed; after the barrier,
-    // every wave's have, and nobody reads this stage any more.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   };
   int g = 0;
   for (; g + 2 <= G; g += 2) {

@@ -212,6 +212,22 @@ def test_w4a8_ragged_shapes(qg, M, K, N):
     _w4a8_check(qg, x, codes, scales, window=(0, M, 0, N))
 
 
+@pytest.mark.parametrize("M,K,N", [(130, 640, 272), (257, 1152, 400), (192, 1664, 160)])
+def test_w4a8_large_kernel_back_to_back_bias_windows(qg, M, K, N):
+    """M > 64 runs the large-M kernel, which takes the accumulated bias off
+    every 4 groups and after the last one.  With G = 1 (mod 4) groups two
+    windows end in consecutive groups; their column sums sit in alternating
+    LDS buffers.  The production call against the oracle, the debug call's
+    partials, and the two calls' outputs bit-identical."""
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M * 7 + K)
+    codes, scales = synth.weights(N, K, seed=N * 7 + K)
+    wp, sp = packed(qg, codes, scales)
+    y = host(qg.w4a8_gemm(dev(x), wp, sp, N))
+    assert_bounds(y, oracle.ref_w4a8(x, codes, scales), f"w4a8 M={M} K={K} N={N}")
+    _, yd = _w4a8_check(qg, x, codes, scales, window=(M - 40, M, 0, N))
+    assert np.array_equal(bits(yd), bits(y))
+
+
 def test_w4a8_all_minus_8_with_negative_scales_and_zero_rows(qg):
     """The pages' failure: signed scales read as unsigned.  Every code -8 and
     every scale negative, plus an all-zero token row."""
