@@ -23,8 +23,10 @@
 //   W4A8   2 x v_mfma_i32_16x16x64_i8 on (16*q_w, q_a) -> 16*P exactly, then
 //          acc += fp32(16*P) * s_w; the token scale at the end carries the
 //          1/16 (a power of two: the same result as scaling each term)
-//   W4A16  4 x v_mfma_f32_16x16x32_f16 on exact fp16 codes q_w and fp16 x,
-//          then acc += group_sum * s_w
+//   W4A16  4 x v_mfma_f32_16x16x32_f16 on the biased fp16 codes (1032 + q_w,
+//          or 1152 + 16 q_w against x / 16) and fp16 x, started from minus
+//          the activations' bias (4 more products with a constant operand,
+//          shared by the stage's n-tiles), then acc += group_sum * s_w
 //   W8A16  as W4A16 with int8 table codes converted exactly to fp16.
 // The k order inside a lane operand is a permutation shared by both operands,
 // so the contraction is unaffected by it.  W4A8 reads its activation codes
@@ -172,6 +174,33 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
                                               const uint16_t* lds_s, f32x4 (&acc)[NT][MT]) {
   const int col = lane & 15, quad = lane >> 4;
   const int gs = gvalid ? g : 0;
+  // fp16 activation operands.  W4A16: the int4 conversion leaves every
+  // weight value biased (see operands.h), so each m-tile's product starts
+  // from minus the bias of its activation columns, formed once per stage by
+  // the matrix core from the constant bias operand and shared by all
+  // n-tiles.  W8A16 converts exactly and starts from zero.
+  f16x8 b[MT][4];
+  f32x4 seed[MT];
+  if constexpr (MODE != kW4A8) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      seed[mt] = (f32x4)0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // W4A16 weight elements come in k order {0,2,4,6,1,3,5,7}; match it.
+        if constexpr (MODE == kW4A16)
+          b[mt][t] = w4_scale_activations(
+              __builtin_shufflevector(st.x[mt][t], st.x[mt][t], 0, 2, 4, 6, 1, 3, 5, 7));
+        else
+          b[mt][t] = st.x[mt][t];
+      }
+      if constexpr (MODE == kW4A16) {
+        const f16x8 c = w4_bias_operand();
+#pragma unroll
+        for (int t = 0; t < 4; ++t) seed[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(c, b[mt][t], seed[mt], 0, 0, 0);
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     uint2 sv;
@@ -208,10 +237,10 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
     } else {
       f16x8 a[4];
       if constexpr (MODE == kW4A16) {
-        a[0] = w4_to_f16x8(st.w[j].x);
-        a[1] = w4_to_f16x8(st.w[j].y);
-        a[2] = w4_to_f16x8(st.w[j].z);
-        a[3] = w4_to_f16x8(st.w[j].w);
+        a[0] = w4_to_f16x8_biased(st.w[j].x);
+        a[1] = w4_to_f16x8_biased(st.w[j].y);
+        a[2] = w4_to_f16x8_biased(st.w[j].z);
+        a[3] = w4_to_f16x8_biased(st.w[j].w);
       } else {
         a[0] = i8_to_f16x8(st.w[j][0].x, st.w[j][0].y);
         a[1] = i8_to_f16x8(st.w[j][0].z, st.w[j][0].w);
@@ -220,19 +249,10 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        f16x8 b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // W4A16 weight elements come in k order {0,2,4,6,1,3,5,7}; match it.
-          if constexpr (MODE == kW4A16)
-            b[t] = __builtin_shufflevector(st.x[mt][t], st.x[mt][t], 0, 2, 4, 6, 1, 3, 5, 7);
-          else
-            b[t] = st.x[mt][t];
-        }
-        f32x4 gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[0], (f32x4)0.0f, 0, 0, 0);
-        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b[1], gs, 0, 0, 0);
-        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], b[2], gs, 0, 0, 0);
-        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], b[3], gs, 0, 0, 0);
+        f32x4 gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], b[mt][0], seed[mt], 0, 0, 0);
+        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], b[mt][1], gs, 0, 0, 0);
+        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[2], b[mt][2], gs, 0, 0, 0);
+        gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[3], b[mt][3], gs, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][mt][r] = __builtin_fmaf(gs[r], (float)sc[r], acc[j][mt][r]);
       }

@@ -18,14 +18,43 @@ namespace qg {
 // 0x6400 outside the mask and the nibble's top bit inside it, so the
 // sign flip (^ 8), the mask and the exponent insert take one instruction.
 constexpr uint32_t kBitop3MaskXorElse = 0x6A;
-__device__ __forceinline__ f16x8 w4_to_f16x8(uint32_t w) {
+
+// The 8 values before the affine step: 1032 + q in elements 0, 1, 4, 5 and
+// 1152 + 16 q in elements 2, 3, 6, 7 (all exact in fp16).
+__device__ __forceinline__ f16x8 w4_to_f16x8_biased(uint32_t w) {
   const uint32_t y = w >> 8;
   u32x4 p;
   p[0] = __builtin_amdgcn_bitop3_b32(w, 0x000F000Fu, 0x64086408u, kBitop3MaskXorElse);
   p[1] = __builtin_amdgcn_bitop3_b32(w, 0x00F000F0u, 0x64806480u, kBitop3MaskXorElse);
   p[2] = __builtin_amdgcn_bitop3_b32(y, 0x000F000Fu, 0x64086408u, kBitop3MaskXorElse);
   p[3] = __builtin_amdgcn_bitop3_b32(y, 0x00F000F0u, 0x64806480u, kBitop3MaskXorElse);
-  const f16x8 v = __builtin_bit_cast(f16x8, p);
+  return __builtin_bit_cast(f16x8, p);
+}
+
+// The activation operand that goes with the biased int4 values: elements
+// 2, 3, 6, 7 (words 1 and 3) divided by 16, exact for every normal fp16
+// quotient.  Then x * (1152 + 16 q) / 16 = 72 x + q x and x * (1032 + q) =
+// 1032 x + q x: the contraction is sum(q x) plus a bias that depends on the
+// activations alone (w4_bias_operand), which the product takes off by
+// starting from minus that bias.
+//
+// A whole-vector multiply (the compiler drops the factors of 1): taking
+// words 1 and 3 out with __builtin_bit_cast(f16x2, u[i]) made the compiler
+// read word 0 for both.
+__device__ __forceinline__ f16x8 w4_scale_activations(f16x8 x) {
+  const f16x8 m = {1.0f16, 1.0f16, 0.0625f16, 0.0625f16, 1.0f16, 1.0f16, 0.0625f16, 0.0625f16};
+  return x * m;
+}
+
+// A operand whose every row holds the biases with the sign flipped (-1032,
+// -1152 in the slots above): its product with the scaled activations is
+// minus the bias of each activation column, in all four rows of a lane.
+__device__ __forceinline__ f16x8 w4_bias_operand() {
+  return f16x8{-1032.0f16, -1032.0f16, -1152.0f16, -1152.0f16, -1032.0f16, -1032.0f16, -1152.0f16, -1152.0f16};
+}
+
+__device__ __forceinline__ f16x8 w4_to_f16x8(uint32_t w) {
+  const f16x8 v = w4_to_f16x8_biased(w);
   const f16x8 mul = {1.0f16, 1.0f16, 0.0625f16, 0.0625f16, 1.0f16, 1.0f16, 0.0625f16, 0.0625f16};
   const f16x8 add = {-1032.0f16, -1032.0f16, -72.0f16, -72.0f16, -1032.0f16, -1032.0f16, -72.0f16, -72.0f16};
   return v * mul + add;

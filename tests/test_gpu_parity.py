@@ -438,6 +438,36 @@ def test_w4a16_ragged_shapes(qg, M, K, N):
     assert_bounds(host(y), oracle.ref_w4a16(x, codes, scales))
 
 
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_w4a16_biased_operands_with_extreme_activations(qg, M):
+    """The K-split W4A16 kernel multiplies biased codes (1032 + q, or
+    1152 + 16 q against x / 16) and starts each product from minus the
+    activations' bias.  Activations near the fp16 limit, subnormal ones and
+    zero rows, codes -8 and 7, and weight columns of all-zero codes (whose
+    outputs must stay at rounding level) all stay within the fp16 bounds."""
+    K, N = 1024, 160
+    rng = np.random.default_rng(M + 5)
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M + 70)
+    x[0, ::97] = np.float16(60000.0)
+    x[0, 5::131] = np.float16(-60000.0)
+    x[-1, ::3] = np.float16(2.0 ** -20)        # subnormal, and subnormal again once divided by 16
+    if M > 2:
+        x[1] = 0
+    codes, scales = synth.weights(N, K, seed=M + 71)
+    codes[:16] = -8
+    codes[16:32] = 7
+    codes[32:48] = 0
+    codes[48:64] = rng.choice(np.array([-8, 7], np.int8), size=(16, K))
+    wp, sp = packed(qg, codes, scales)
+    y = host(qg.w4a16_gemm(dev(x), wp, sp, N))
+    ref = oracle.ref_w4a16(x, codes, scales)
+    # row 0 (outputs up to about 2e4) on its own, so that it does not set
+    # the tolerance of the ordinary rows
+    assert_bounds(y[:1], ref[:1], f"w4a16 extreme M={M} row 0")
+    if M > 1:
+        assert_bounds(y[1:], ref[1:], f"w4a16 extreme M={M} rows 1+")
+
+
 # ---------------------------------------------------------------------------
 # int8 vocabulary table: requantisation, gather, lm_head
 # ---------------------------------------------------------------------------
