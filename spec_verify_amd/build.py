@@ -32,8 +32,9 @@ FLAGS = [
 
 # Per-source flags.  The weight-streaming kernels keep their matrix-core
 # results in ordinary VGPRs instead of accumulation registers, which saves a
-# v_accvgpr_read per result element (measured 1-2% on the verify shapes, no
-# change on decode); the wide and prefill kernels measured no gain or a loss.
+# v_accvgpr_read per result element (measured 1-2% faster on the verify
+# shapes, no change on decode, about 1% slower on the int8 draft head); the
+# wide and prefill kernels measured no gain or a loss.
 SOURCE_FLAGS = {"gemm_skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
