@@ -124,7 +124,7 @@ __device__ __forceinline__ uint4 ld128_stream(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxStream));
 }
 
-template <int MODE, int NT, int MT>
+template <int MODE, int NT, int MT, bool SL>
 __device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs, Stage<MODE, NT, MT>& st,
                                            bool valid, int g, int lane, int mt0) {
   const int col = lane & 15, quad = lane >> 4;
@@ -140,7 +140,7 @@ __device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs
       // packed block (n-tile j, group g) and the lane's 4 scales of it
       const uint32_t blk = (uint32_t)j * G + (uint32_t)g;
       st.w[j] = ld128_stream(rs.w, (blk * 64u + lane) * 16u + bad);
-      if constexpr (MODE == kW4A8)
+      if constexpr (MODE == kW4A8 && !SL)
         st.sc[j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.s, (blk * 16u + 4u * quad) * 2u + bad, 0, 0));
     }
   }
@@ -162,13 +162,15 @@ __device__ __forceinline__ void load_stage(const SkinnyParams& p, const Rsrc& rs
   }
 }
 
-// Group scales: W4A8 stages carry them (fp16, fed to v_fma_mix as they
-// are); W4A16 and W8A16 read them from LDS, stored there as [group][column
-// of the workgroup], where a stage past the wave's last group reads group
-// 0's (its products are zero).  W4A8 sums fp32(16 P) * s: the factor 16 of
-// the 16*q weights is removed with the token scale at the end (an exact
-// power of two, so the result is the same as scaling every term).
-template <int MODE, int NT, int MT, bool DEBUG>
+// Group scales, fed to v_fma_mix as fp16.  W4A8 reads them from LDS in
+// their memory layout, [n-tile][group][16 columns] (SL), or, when K is too
+// long for that, from the stage, which then carries them.  W4A16 and W8A16
+// read them from LDS, stored there as [group][column of the workgroup].  A
+// stage past the wave's last group reads group 0's (its products are zero).
+// W4A8 sums fp32(16 P) * s: the factor 16 of the 16*q weights is removed
+// with the token scale at the end (an exact power of two, so the result is
+// the same as scaling every term).
+template <int MODE, int NT, int MT, bool DEBUG, bool SL>
 __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage<MODE, NT, MT>& st, int g,
                                               bool gvalid, int nt0, int nvalid, int mt0, int lane,
                                               const uint16_t* lds_s, f32x4 (&acc)[NT][MT]) {
@@ -204,8 +206,10 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     uint2 sv;
-    if constexpr (MODE == kW4A8)
+    if constexpr (MODE == kW4A8 && !SL)
       sv = st.sc[j];
+    else if constexpr (MODE == kW4A8)
+      sv = *reinterpret_cast<const uint2*>(lds_s + (j * p.G + gs) * 16 + 4 * quad);
     else
       sv = *reinterpret_cast<const uint2*>(lds_s + gs * (16 * NT) + j * 16 + 4 * quad);
     const _Float16 sc[4] = {__builtin_bit_cast(_Float16, (uint16_t)(sv.x & 0xFFFFu)),
@@ -262,20 +266,23 @@ __device__ __forceinline__ void compute_stage(const SkinnyParams& p, const Stage
 
 // Epilogue of both weight-streaming kernels: the waves' fp32 sums meet in
 // LDS (red, 2 x NW x QC x 64 f32x4 when the tiles take several chunks) and
-// are added in wave order, then stored as fp16.
-template <int NT, int MT, int NW>
+// are added in wave order, then stored as fp16.  W4A8 (one m-tile, at most
+// 40 KiB of sums) takes them in one chunk, so one barrier; the fp16 kernels
+// keep their buffers within 32 KiB, which leaves LDS for their scales and a
+// second workgroup per CU.
+template <int MODE, int NT, int MT, int NW>
 constexpr int red_chunk() {
-  return NT * MT * NW <= 32 ? NT * MT : 32 / NW;
+  return MODE == kW4A8 || NT * MT * NW <= 32 ? NT * MT : 32 / NW;
 }
-template <int NT, int MT, int NW>
+template <int MODE, int NT, int MT, int NW>
 constexpr int red_bufs() {
-  return (NT * MT + red_chunk<NT, MT, NW>() - 1) / red_chunk<NT, MT, NW>() > 1 ? 2 : 1;
+  return (NT * MT + red_chunk<MODE, NT, MT, NW>() - 1) / red_chunk<MODE, NT, MT, NW>() > 1 ? 2 : 1;
 }
 
 template <int MODE, int NT, int MT, int NW>
 __device__ __forceinline__ void sum_and_store(const SkinnyParams& p, const f32x4 (&acc)[NT][MT], int nt0, int mt0,
                                               int nvalid, int wave, int lane,
-                                              f32x4 (*red)[NW][red_chunk<NT, MT, NW>()][64]) {
+                                              f32x4 (*red)[NW][red_chunk<MODE, NT, MT, NW>()][64]) {
   // Sum over the waves in wave order, QC (n-tile, m-tile) tiles at a time:
   // every wave parks its f32x4 per lane and tile in LDS, one barrier, then
   // thread t of a tile adds the 4 columns 4 (t % 4) .. + 3 of row t / 4 over
@@ -285,7 +292,7 @@ __device__ __forceinline__ void sum_and_store(const SkinnyParams& p, const f32x4
   // fall in distinct LDS banks.  Two buffers alternate (one barrier per
   // chunk); nothing is stored to global memory before the last barrier.
   constexpr int Q = NT * MT;                                  // tiles per wave
-  constexpr int QC = Q * NW <= 32 ? Q : 32 / NW;              // tiles per chunk: <= 32 KiB per buffer
+  constexpr int QC = red_chunk<MODE, NT, MT, NW>();            // tiles per chunk
   constexpr int NCH = (Q + QC - 1) / QC;
   const int tid = (int)threadIdx.x;
   constexpr int KPC = (QC * 64 + 64 * NW - 1) / (64 * NW);     // sums per thread per chunk
@@ -332,7 +339,7 @@ __device__ __forceinline__ void sum_and_store(const SkinnyParams& p, const f32x4
     }
 }
 
-template <int MODE, int NT, int MT, int NW, int PF, bool DEBUG>
+template <int MODE, int NT, int MT, int NW, int PF, bool DEBUG, bool SL>
 __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
@@ -373,12 +380,14 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
     rs.s = make_rsrc(p.s + (int64_t)nt0 * G * 16, (uint32_t)(nvalid * G * 32));
   }
 
-  // W4A16 / W8A16: the workgroup's group scales (NT*16 columns x G groups,
-  // one contiguous block in both scale layouts) go to LDS once, transposed
-  // to [group][column]; the loads are issued before the weight prefetch so
-  // the barrier below waits for them only.  (W4A8 stages carry their scales
-  // instead, one 8-byte load per n-tile and group: the decode kernel then
-  // starts multiplying as soon as its first stage lands.)
+  // The workgroup's group scales (NT*16 columns x G groups, one contiguous
+  // block in both scale layouts) go to LDS once.  W4A16 / W8A16: through
+  // registers, transposed to [group][column]; the loads are issued before
+  // the weight prefetch so the barrier below waits for them only.  W4A8
+  // (SL): as they lie in memory, by LDS-direct loads of 1 KiB per wave
+  // issued before the first stage, so they travel with it; this takes the
+  // small scale loads (one per n-tile and group) off the load path that
+  // bounds the decode kernel.
   extern __shared__ __attribute__((aligned(16))) uint16_t lds_s[];
   constexpr int COLS = 16 * NT;
   constexpr int SPT = 8;                       // scales per thread per pass (one 16-byte load)
@@ -408,6 +417,12 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
       }
     }
   }
+  if constexpr (MODE == kW4A8 && SL) {
+    const int nchunk = (nvalid * p.G * 32 + 1023) >> 10;   // the dynamic LDS holds ceil(NT G 32 / 1024) KiB
+    for (int c = wave; c < nchunk; c += NW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.s, (lds_ptr_t)(lds_s + c * 512), 16, (uint32_t)lane * 16u,
+                                               (uint32_t)c * 1024u, 0, 0);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // This wave's groups are wave, wave + NW, ...; PF of them are in flight in
@@ -427,8 +442,20 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
   Stage<MODE, NT, MT> st[PF];
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
-    load_stage<MODE, NT, MT>(p, rs, st[s], s < ng, gidx(s), lane, mt0);
+    load_stage<MODE, NT, MT, SL>(p, rs, st[s], s < ng, gidx(s), lane, mt0);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (MODE == kW4A8 && SL) {
+    // Loads complete in order: once no more than the ring's own loads are
+    // outstanding, this wave's scale chunks are in LDS.  A bare barrier
+    // between compiler fences then publishes them; a release fence would
+    // also wait for the ring.
+    constexpr int kRing = PF * (NT + 2 * MT);
+    static_assert(kRing < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((kRing & 15) | ((kRing >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
   if constexpr (MODE != kW4A8) {
 #pragma unroll
@@ -452,10 +479,10 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int ii = r * PF + s;
-      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), true, nt0, nvalid, mt0, lane, lds_s, acc);
+      compute_stage<MODE, NT, MT, DEBUG, SL>(p, st[s], gidx(ii), true, nt0, nvalid, mt0, lane, lds_s, acc);
       // Stages past the last group load nothing (out-of-range offsets) and
       // multiply zeros, which keeps this loop free of branches.
-      load_stage<MODE, NT, MT>(p, rs, st[s], ii + PF < ng, gidx(ii + PF), lane, mt0);
+      load_stage<MODE, NT, MT, SL>(p, rs, st[s], ii + PF < ng, gidx(ii + PF), lane, mt0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -463,11 +490,11 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int ii = (rounds - 1) * PF + s;
-      compute_stage<MODE, NT, MT, DEBUG>(p, st[s], gidx(ii), ii < ng, nt0, nvalid, mt0, lane, lds_s, acc);
+      compute_stage<MODE, NT, MT, DEBUG, SL>(p, st[s], gidx(ii), ii < ng, nt0, nvalid, mt0, lane, lds_s, acc);
     }
   }
 
-  __shared__ f32x4 red[red_bufs<NT, MT, NW>()][NW][red_chunk<NT, MT, NW>()][64];
+  __shared__ f32x4 red[red_bufs<MODE, NT, MT, NW>()][NW][red_chunk<MODE, NT, MT, NW>()][64];
   sum_and_store<MODE, NT, MT, NW>(p, acc, nt0, mt0, nvalid, wave, lane, red);
 }
 
@@ -483,28 +510,49 @@ constexpr int prefetch_depth() {
   return MODE == kW4A8 ? (NT * MT <= 4 ? 5 : 3) : 2;
 }
 
+// W4A8 group scales staged in LDS: the bytes the kernel's LDS-direct loads
+// fill (whole KiB), or 0 when K is too long for the budget, in which case
+// the stages carry the scales.
+constexpr size_t kScaleLdsMax = 32768;
+inline size_t w4a8_scale_lds(int nt, int G) {
+  const size_t b = ((size_t)32 * nt * G + 1023) / 1024 * 1024;
+  return b <= kScaleLdsMax ? b : 0;
+}
+
 template <int MODE, int NT, int NW, bool DEBUG>
 void launch_mt(const SkinnyParams& p, int mt, dim3 grid, hipStream_t st) {
   const dim3 block(64 * NW);
-  // the workgroup's group scales (W4A16 / W8A16 only; K <= 65536 keeps
-  // this within 64 KiB)
-  const size_t lds = MODE == kW4A8 ? 0 : (size_t)16 * NT * p.G * 2;
-  switch (mt) {
-    case 1: skinny_kernel<MODE, NT, 1, NW, prefetch_depth<MODE, NT, 1>(), DEBUG><<<grid, block, lds, st>>>(p); break;
-    case 2: skinny_kernel<MODE, NT, 2, NW, prefetch_depth<MODE, NT, 2>(), DEBUG><<<grid, block, lds, st>>>(p); break;
-    case 3: skinny_kernel<MODE, NT, 3, NW, prefetch_depth<MODE, NT, 3>(), DEBUG><<<grid, block, lds, st>>>(p); break;
-    default: skinny_kernel<MODE, NT, 4, NW, prefetch_depth<MODE, NT, 4>(), DEBUG><<<grid, block, lds, st>>>(p); break;
+  if constexpr (MODE == kW4A8) {
+    // M <= 16 here (larger W4A8 batches take the row split): one m-tile
+    (void)mt;
+    constexpr int PF = prefetch_depth<MODE, NT, 1>();
+    if (const size_t lds = w4a8_scale_lds(NT, p.G))
+      skinny_kernel<MODE, NT, 1, NW, PF, DEBUG, true><<<grid, block, lds, st>>>(p);
+    else
+      skinny_kernel<MODE, NT, 1, NW, PF, DEBUG, false><<<grid, block, 0, st>>>(p);
+  } else {
+    // the workgroup's group scales (K <= 65536 keeps this within 64 KiB)
+    const size_t lds = (size_t)16 * NT * p.G * 2;
+    switch (mt) {
+      case 1: skinny_kernel<MODE, NT, 1, NW, prefetch_depth<MODE, NT, 1>(), DEBUG, false><<<grid, block, lds, st>>>(p); break;
+      case 2: skinny_kernel<MODE, NT, 2, NW, prefetch_depth<MODE, NT, 2>(), DEBUG, false><<<grid, block, lds, st>>>(p); break;
+      case 3: skinny_kernel<MODE, NT, 3, NW, prefetch_depth<MODE, NT, 3>(), DEBUG, false><<<grid, block, lds, st>>>(p); break;
+      default: skinny_kernel<MODE, NT, 4, NW, prefetch_depth<MODE, NT, 4>(), DEBUG, false><<<grid, block, lds, st>>>(p); break;
+    }
   }
 }
 
+// Two n-tiles per workgroup only for W4A8 (skinny_plan); every mode takes
+// four on wide outputs.
 template <int MODE, bool DEBUG>
 hipError_t launch_mode(const SkinnyParams& p, const SkinnyPlan& pl, int mt, dim3 grid, hipStream_t st) {
-  if (pl.nt == 1)
-    launch_mt<MODE, 1, 8, DEBUG>(p, mt, grid, st);
-  else if (pl.nt == 2)
-    launch_mt<MODE, 2, 8, DEBUG>(p, mt, grid, st);
-  else
-    launch_mt<MODE, 4, 4, DEBUG>(p, mt, grid, st);
+  if constexpr (MODE == kW4A8) {
+    if (pl.nt == 2) {
+      launch_mt<MODE, 2, 8, DEBUG>(p, mt, grid, st);
+      return hipGetLastError();
+    }
+  }
+  launch_mt<MODE, 4, 4, DEBUG>(p, mt, grid, st);
   return hipGetLastError();
 }
 
@@ -551,18 +599,25 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   // one XCD) instead of 327 KB of codes and 82 KB of weights for two
   // n-tiles x 64 rows, and the loads it keeps in flight stay few; the CU's
   // limit on outstanding L2 requests is what bounds this GEMM.  Measured at
-  // M = 64, K = N = 5120: 8.7 us, against 10.3 us for an LDS-slab kernel of
-  // two n-tiles x 64 rows with every load in flight at once and 10.9 us for
-  // the streaming kernel's two n-tiles x 64 rows.  The debug window runs the
+  // M = 64, K = N = 5120: 8.2 us (8.8 us with the scales carried by the
+  // stages and a two-barrier reduction), against 10.3 us for an LDS-slab
+  // kernel of two n-tiles x 64 rows with every load in flight at once and
+  // 10.9 us for the streaming kernel's two n-tiles x 64 rows.  A deeper or
+  // earlier-issued ring is slower (9.2-9.7 us).  The debug window runs the
   // same kernel, instantiated with the partial-sum stores.
   if (a.mode == kW4A8 && a.M > 16) {
     p.ms = (p.M + 15) / 16;
     p.wgs = (p.N / 16 + kMsplitNT - 1) / kMsplitNT;
     const dim3 grid((unsigned)(p.wgs * p.ms));
-    if (a.dbg)
-      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, true><<<grid, dim3(512), 0, st>>>(p);
+    const size_t lds = w4a8_scale_lds(kMsplitNT, p.G);
+    if (a.dbg && lds)
+      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, true, true><<<grid, dim3(512), lds, st>>>(p);
+    else if (a.dbg)
+      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, true, false><<<grid, dim3(512), 0, st>>>(p);
+    else if (lds)
+      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false, true><<<grid, dim3(512), lds, st>>>(p);
     else
-      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false><<<grid, dim3(512), 0, st>>>(p);
+      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false, false><<<grid, dim3(512), 0, st>>>(p);
     return hipGetLastError();
   }
   const SkinnyPlan pl = skinny_plan(a.mode, a.N, a.K);

@@ -191,6 +191,27 @@ def test_w4a8_row_split_shapes(qg, M, K, N):
     assert np.array_equal(bits(yd), bits(y))
 
 
+@pytest.mark.parametrize("M,K,N", [(40, 32768, 96), (9, 66048, 48), (2, 32896, 16400)])
+def test_w4a8_scales_past_the_lds_budget(qg, M, K, N):
+    """K long enough that a workgroup's group scales exceed the 32 KiB the
+    weight-streaming kernel stages in LDS, so its stages carry them instead:
+    the row split (16 < M <= 64), and two and four n-tiles per workgroup
+    (M <= 16, N / 16 up to and past 1024).  The production call against the
+    oracle (sampled columns on the wide case), and the debug call's partials
+    on a window with its y bit-identical to the production call's."""
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M * 7 + K)
+    codes, scales = synth.weights(N, K, seed=N * 7 + K)
+    wp, sp = packed(qg, codes, scales)
+    y = host(qg.w4a8_gemm(dev(x), wp, sp, N))
+    cols = np.arange(N) if N <= 1024 else np.unique(np.concatenate([np.arange(0, N, 97), np.arange(N - 16, N)]))
+    assert_bounds(y[:, cols], oracle.ref_w4a8(x, codes[cols], scales[cols]), f"w4a8 M={M} K={K} N={N}")
+    n0, n1 = max(0, N // 2 - 40), min(N, N // 2 + 56)
+    yd, _, _, P = qg.w4a8_gemm_debug(dev(x), wp, sp, N, window=(0, M, n0, n1))
+    oq, _ = oracle.quant_act(x)
+    assert np.array_equal(host(P).astype(np.int64), oracle.partials(oq, codes[n0:n1])), "int32 partials"
+    assert np.array_equal(bits(host(yd)), bits(y))
+
+
 @pytest.mark.slow
 def test_w4a8_prefill_workload_sampled(qg):
     cfg = synth.CONFIGS["prefill_w4a8"]
