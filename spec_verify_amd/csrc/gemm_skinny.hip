@@ -47,7 +47,8 @@ struct SkinnyParams {
   int M, N, K, G;
   int ms;                   // m-groups: workgroups that share an n-block, each with MT m-tiles
   int wgs;                  // n-blocks of unequal size (0: NT tiles each): block b has tiles
-                            // [b T / wgs, (b + 1) T / wgs) of the T n-tiles
+                            // [b T / wgs, (b + 1) T / wgs) of the T n-tiles, or, with t1,
+  int t1;                   // the first wgs / 2 blocks share tiles [0, t1) and the rest [t1, T)
   uint16_t* y;
   int32_t* dbg;
   int dm0, dm1, dn0, dn1;
@@ -355,9 +356,17 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
     nb = (int)(lin / (unsigned)p.ms);
     mg = (int)(lin % (unsigned)p.ms);
   }
-  const int nt0 = p.wgs ? (int)((int64_t)nb * (p.N / 16) / p.wgs) : nb * NT;
+  int nt0, nvalid;
+  if (p.t1) {
+    const int half = p.wgs / 2, T = p.N / 16;
+    const int lo = nb < half ? 0 : p.t1, cnt = nb < half ? p.t1 : T - p.t1, b = nb < half ? nb : nb - half;
+    nt0 = lo + (int)((int64_t)b * cnt / half);
+    nvalid = lo + (int)((int64_t)(b + 1) * cnt / half) - nt0;
+  } else {
+    nt0 = p.wgs ? (int)((int64_t)nb * (p.N / 16) / p.wgs) : nb * NT;
+    nvalid = p.wgs ? (int)((int64_t)(nb + 1) * (p.N / 16) / p.wgs) - nt0 : min(NT, p.N / 16 - nt0);
+  }
   const int mt0 = mg * MT;
-  const int nvalid = p.wgs ? (int)((int64_t)(nb + 1) * (p.N / 16) / p.wgs) - nt0 : min(NT, p.N / 16 - nt0);
 
   f32x4 acc[NT][MT];
 #pragma unroll
@@ -591,6 +600,7 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.dm0 = (int)a.dm0; p.dm1 = (int)a.dm1; p.dn0 = (int)a.dn0; p.dn1 = (int)a.dn1;
   p.ms = 1;
   p.wgs = 0;
+  p.t1 = 0;
   // W4A8 at 16 < M <= 64 (decode batches): one 16-row m-tile and at most
   // 5 n-tiles per workgroup (the n-tiles dealt into ceil(T / 5) balanced
   // blocks of 4 or 5), 8 waves splitting K, a one-stage ring.  Each CU then
@@ -626,9 +636,18 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   // projections, the draft head): blocks of four n-tiles leave some CUs
   // with one workgroup more than the rest (544 workgroups for N = 34,816),
   // and those set the time; 512 blocks of four or five tiles give every CU
-  // two.
+  // two.  The two are blocks b and b + 256, and the older one's waves issue
+  // first: with equal blocks, per-workgroup timestamps at N = 34,816, M = 8
+  // put the first 256 blocks' ends at a median of 13.6 us and the others'
+  // at 16.6 us, the CU then running one workgroup alone.  The first 256
+  // blocks therefore take 10/17 of the tiles, at most 5 each (5 against 3.5
+  // tiles at that N; verify 18.8 -> 18.1 us at M = 8, 22.2 -> 21.2 us at
+  // M = 16; 6 against 2.5 and 7 against 1.5 were slower).  Any split is a
+  // partition of the tiles, so results do not depend on where the
+  // workgroups land.
   if (a.mode != kW4A8 && a.dbg == nullptr && pl.nt == 4 && p.N / 16 > 1024 && p.N / 16 <= 5 * kBalancedWgs) {
     p.wgs = kBalancedWgs;
+    p.t1 = std::min((int)((int64_t)(p.N / 16) * 10 / 17), 5 * (kBalancedWgs / 2));
     if (a.mode == kW4A16)
       launch_mt<kW4A16, 5, 4, false>(p, mt, dim3((unsigned)kBalancedWgs), st);
     else

@@ -449,7 +449,10 @@ def test_w4a16_verify_workload_full(qg, name):
                                    # n-tiles on, a last workgroup with one valid n-tile; M <= 32:
                                    # the K-split kernel on many workgroups)
                                    (5, 384, 32784), (33, 256, 32784), (64, 128, 131088), (3, 256, 131072),
-                                   (64, 128, 196624), (40, 256, 196608)])
+                                   (64, 128, 196624), (40, 256, 196608),
+                                   # 1025 and 2560 n-tiles: the 512 balanced blocks, split unevenly
+                                   # between the first and second 256 and evenly at the top
+                                   (2, 256, 16400), (16, 128, 40960)])
 def test_w4a16_ragged_shapes(qg, M, K, N):
     x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M * 3 + K)
     codes, scales = synth.weights(N, K, seed=N * 3 + K)
@@ -510,7 +513,7 @@ def test_gather_bit_exact_with_out_of_range_ids(qg):
     assert np.array_equal(bits(host(out)), bits(oracle.ref_gather(ids, oQ, oS)))
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (64, 640, 400), (8, 256, 1040), (70, 256, 64),
+@pytest.mark.parametrize("M,K,N", [(1, 128, 16), (64, 640, 400), (8, 256, 1040), (70, 256, 64), (8, 256, 16400),
                                    # wide outputs (see the W4A16 cases)
                                    (40, 384, 32784), (9, 128, 131088), (64, 256, 32768), (48, 128, 131088),
                                    (33, 256, 196624), (64, 128, 196624)])
