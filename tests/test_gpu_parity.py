@@ -191,10 +191,14 @@ def test_w4a8_row_split_shapes(qg, M, K, N):
     assert np.array_equal(bits(yd), bits(y))
 
 
-@pytest.mark.parametrize("M,K,N", [(40, 32768, 96), (9, 66048, 48), (2, 32896, 16400)])
+@pytest.mark.parametrize("M,K,N", [(40, 32768, 96), (9, 66048, 48), (2, 32896, 16400),
+                                   # just inside the budget: 32 KiB of scales beside the row
+                                   # split's 40 KiB of partial sums (72 KiB of LDS)
+                                   (40, 25600, 96)])
 def test_w4a8_scales_past_the_lds_budget(qg, M, K, N):
     """K long enough that a workgroup's group scales exceed the 32 KiB the
-    weight-streaming kernel stages in LDS, so its stages carry them instead:
+    weight-streaming kernel stages in LDS, so its stages carry them instead
+    (and one shape just inside that budget):
     the row split (16 < M <= 64), and two and four n-tiles per workgroup
     (M <= 16, N / 16 up to and past 1024).  The production call against the
     oracle (sampled columns on the wide case), and the debug call's partials
