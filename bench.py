@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB device copy that calibrates the FETCH_SIZE / WRITE_SIZE "
                          "counters (run it under rocprofv3 --pmc), then exit")
+    ap.add_argument("--floor", action="store_true",
+                    help="only time the load floors of the decode GEMM's operand walk (qg_probe_read: "
+                         "a plain read of its weights, its own access pattern, an empty launch), then exit")
     return ap.parse_args()
 
 
@@ -77,6 +80,42 @@ def copy_calibration():
         c.fill_(3)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+
+
+def load_floor():
+    """Per-launch times, in a replayed graph, of reads with the decode GEMM's
+    operand walk and none of its arithmetic (qg_probe_read): its packed
+    weights (13,107,200 B, rotated over copies past the Infinity Cache) read
+    as 256 contiguous slices, then as the row split reads them (64 n-block
+    slices, each read by its four m-groups on one XCD, plus each m-group's
+    quarter of the 327,680 B of codes), and a launch of that grid that reads
+    nothing."""
+    import torch
+    import spec_verify_amd as qg
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS["decode_w4a8"]
+    K, N = cfg["K"], cfg["N"]
+    wbytes = N * K // 2
+    n = copies_for(wbytes)
+    w = [torch.full((wbytes,), 3, dtype=torch.uint8, device=dev) for _ in range(n)]
+    codes = torch.full((cfg["M"] * K,), 5, dtype=torch.uint8, device=dev)
+    none = torch.empty((0,), dtype=torch.uint8, device=dev)
+    sink = torch.empty((256 * 640 // 64,), dtype=torch.int32, device=dev)
+    cases = {
+        "empty_launch_256x512": lambda i: qg.qg_probe_read(none, None, 1, 256, 512, True, sink),
+        "plain_weights_256x640": lambda i: qg.qg_probe_read(w[i % n], None, 1, 256, 640, True, sink),
+        "decode_walk_weights_256x512": lambda i: qg.qg_probe_read(w[i % n], None, 4, 256, 512, True, sink),
+        "decode_walk_256x512": lambda i: qg.qg_probe_read(w[i % n], codes, 4, 256, 512, True, sink),
+        "decode_walk_hot_256x512": lambda i: qg.qg_probe_read(w[0], codes, 4, 256, 512, True, sink),
+    }
+    out = {}
+    for name, fn in cases.items():
+        us, _ = graph_time_us(torch, fn, 200, reps=3)
+        out[name] = round(us, 3)
+        print(f"# floor: {name} {out[name]} us", file=sys.stderr, flush=True)
+    print(json.dumps({"load_floor_us_per_launch": out, "weight_bytes": wbytes, "code_bytes": cfg["M"] * K,
+                      "weight_copies": n}))
 
 
 def gemm_bytes(M, K, N):
@@ -212,6 +251,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.floor:
+        load_floor()
         return
 
     import numpy as np

@@ -327,6 +327,26 @@ int w4a8_gemm_noalloc(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_
  */
 int qg_selftest_quant_division(unsigned long long* counts, void* stream);
 
+/*
+ * qg_probe_read -- diagnostic read with the access pattern of a weight-
+ * streaming GEMM and none of its arithmetic: the load floor its kernels are
+ * measured against (bench.py --floor times it).  Workgroup b of `wgs`
+ * (with `threads` threads, a multiple of 64 up to 1024) reads:
+ *   slice lin / share of a, where a's a_bytes are dealt into wgs / share
+ *     equal slices, with the non-temporal hint when `nontemporal` != 0;
+ *   slice lin % share of c, c's c_bytes dealt into share slices;
+ * lin being b walked as the row-split W4A8 decode kernel walks its grid
+ * (when wgs is a multiple of 8 and wgs / 8 of share, the `share`
+ * workgroups reading one slice of a are consecutive on one XCD).  Each
+ * thread issues its 16-byte loads 16 at a time, its slice of a first; the
+ * only store is one
+ * checksum word per wave into sink (device memory, wgs * threads / 64
+ * uint32).  a and c are read-only and may alias.  share >= 1, wgs a
+ * multiple of share, wgs <= 65536; each slice under 2 GiB.  One launch.
+ */
+int qg_probe_read(const void* a, int64_t a_bytes, const void* c, int64_t c_bytes, int share, int wgs, int threads,
+                  int nontemporal, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

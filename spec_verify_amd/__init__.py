@@ -11,7 +11,7 @@ act_quant_int8, w4_repack, w4a16_gemm, w4a8_gemm, w4a8_prepare, rmsnorm_w4a8_pre
 verify_attention_f16, sample_topk_topp,
 w4a8_gemm_prepared, w4a8_gemm_debug,
 w8a16_gemm, embed_gather_dequant_int8, quant_table_int8, the self-test
-qg_selftest_quant_division, plus the size helpers w4_packed_bytes,
+qg_selftest_quant_division, the diagnostic read qg_probe_read, plus the size helpers w4_packed_bytes,
 w4_scales_bytes, qg_workspace_bytes and qg_status_string.
 """
 from __future__ import annotations
@@ -66,6 +66,7 @@ _SIGS = {
     "embed_gather_dequant_int8": (ctypes.c_int, [_p, _i64, _p, _p, _i64, _i64, _p, _p]),
     "quant_table_int8": (ctypes.c_int, [_p, _i64, _i64, _p, _p, _p]),
     "qg_selftest_quant_division": (ctypes.c_int, [_p, _p]),
+    "qg_probe_read": (ctypes.c_int, [_p, _i64, _p, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _p, _p]),
     "w4a8_noalloc_scratch_bytes": (_sz, []),
     "w4a8_gemm_noalloc": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _p, _p, _p]),
 }
@@ -325,6 +326,18 @@ def quant_table_int8(src_bf16, Q=None, S=None):
     _check("quant_table_int8", lib.quant_table_int8(_ptr(src_bf16), V, H, _ptr(Q), _ptr(S),
                                                     _stream(src_bf16.device)))
     return Q, S
+
+
+def qg_probe_read(a, c=None, share=1, wgs=256, threads=512, nontemporal=True, sink=None):
+    """Run the library's diagnostic read over the device tensors a (and c)
+    with the given split (see qg_probe_read in qgemm.h); returns the sink."""
+    import torch
+    if sink is None:
+        sink = torch.empty((wgs * threads // 64,), dtype=torch.int32, device=a.device)
+    c_ptr, c_bytes = (None, 0) if c is None else (_ptr(c), c.numel() * c.element_size())
+    _check("qg_probe_read", lib.qg_probe_read(_ptr(a), a.numel() * a.element_size(), c_ptr, c_bytes, share, wgs,
+                                              threads, 1 if nontemporal else 0, _ptr(sink), _stream(a.device)))
+    return sink
 
 
 def qg_selftest_quant_division(device=None):

@@ -500,6 +500,19 @@ int qg_selftest_quant_division(unsigned long long* counts, void* stream) {
   return launch_status(qg::launch_quant_division_check(counts, as_stream(stream)));
 }
 
+int qg_probe_read(const void* a, int64_t a_bytes, const void* c, int64_t c_bytes, int share, int wgs, int threads,
+                  int nontemporal, uint32_t* sink, void* stream) {
+  if (a_bytes < 0 || c_bytes < 0 || (a_bytes > 0 && !a) || (c_bytes > 0 && !c) || !sink) return QG_ERR_INVALID_ARG;
+  if (share < 1 || wgs < share || wgs % share || wgs > 65536 || threads < 64 || threads > 1024 || threads % 64)
+    return QG_ERR_INVALID_ARG;
+  // every slice must fit one buffer resource (byte offsets below 2^31)
+  if (a_bytes / (wgs / share) >= ((int64_t)1 << 31) - 16 || c_bytes / share >= ((int64_t)1 << 31) - 16)
+    return QG_ERR_UNSUPPORTED_SHAPE;
+  clear_stale_error();
+  return launch_status(qg::launch_probe_read(a, a_bytes, c, c_bytes, share, wgs, threads, nontemporal != 0, sink,
+                                             as_stream(stream)));
+}
+
 int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H, int8_t* Q, void* S_f16, void* stream) {
   if (V <= 0 || H <= 0) return QG_ERR_INVALID_ARG;
   if (H % kGroup || V > kMaxDim || H > kMaxDim) return QG_ERR_UNSUPPORTED_SHAPE;

@@ -110,6 +110,8 @@ hipError_t launch_quant_table(const uint16_t* src, int64_t V, int64_t H, int8_t*
 // Exhaustive check of the quantiser's division: adds the pairs checked to
 // counts[0] and the mismatches to counts[1].
 hipError_t launch_quant_division_check(unsigned long long* counts, hipStream_t st);
+hipError_t launch_probe_read(const void* a, int64_t a_bytes, const void* c, int64_t c_bytes, int share, int wgs,
+                             int threads, bool nt, uint32_t* sink, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Device helpers

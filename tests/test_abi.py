@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(qg.lib, n), n
     assert set(names) == set(qg.EXPORTS)
@@ -207,6 +207,27 @@ def test_sampler_argument_errors():
     assert call_sampler(ws=MIS) == qg.QG_ERR_INVALID_ARG
     # no rows: nothing to do, no pointers needed
     assert call_sampler(R=0, x=None, u=None, out=None, ws=None, wsb=0) == qg.QG_OK
+
+
+def test_probe_read_argument_errors():
+    """The diagnostic read rejects its bad arguments on the host, before any
+    device call."""
+    f = qg.lib.qg_probe_read
+    ok = dict(a=FAKE, ab=1 << 20, c=None, cb=0, share=4, wgs=256, threads=512, nt=1, sink=FAKE)
+
+    def call(**kw):
+        v = dict(ok, **kw)
+        return f(v["a"], v["ab"], v["c"], v["cb"], v["share"], v["wgs"], v["threads"], v["nt"], v["sink"], None)
+    assert call(a=None) == qg.QG_ERR_INVALID_ARG             # bytes without a pointer
+    assert call(c=None, cb=64) == qg.QG_ERR_INVALID_ARG
+    assert call(ab=-1) == qg.QG_ERR_INVALID_ARG
+    assert call(sink=None) == qg.QG_ERR_INVALID_ARG
+    assert call(share=0) == qg.QG_ERR_INVALID_ARG
+    assert call(wgs=258) == qg.QG_ERR_INVALID_ARG            # not a multiple of share
+    assert call(wgs=2, share=4) == qg.QG_ERR_INVALID_ARG
+    assert call(threads=100) == qg.QG_ERR_INVALID_ARG        # not a multiple of 64
+    assert call(threads=1088) == qg.QG_ERR_INVALID_ARG
+    assert call(wgs=4, share=4, ab=1 << 31) == qg.QG_ERR_UNSUPPORTED_SHAPE   # a 2 GiB slice
 
 
 def test_selftest_rejects_bad_counters():
