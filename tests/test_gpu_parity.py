@@ -530,6 +530,46 @@ def test_w8a16_ragged_shapes(qg, M, K, N):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("mode,M,N", [("w4a16", 8, 48), ("w4a16", 40, 48), ("w8a16", 8, 48), ("w8a16", 64, 80)])
+def test_fp16_modes_at_the_longest_k(qg, mode, M, N):
+    """K = 65536, the longest w4a16_gemm and w8a16_gemm accept: a workgroup
+    of four n-tiles holds 48-64 KiB of group scales in LDS (beside 64 KiB of
+    partial sums at M > 32), most of them stored by the passes past the
+    four register-staged ones."""
+    K = 65536
+    x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M * 5 + N)
+    if mode == "w4a16":
+        codes, scales = synth.weights(N, K, seed=N * 5 + M)
+        codes[:, :128] = -8
+        wp, sp = packed(qg, codes, scales)
+        y = qg.w4a16_gemm(dev(x), wp, sp, N)
+        ref = oracle.ref_w4a16(x, codes, scales)
+    else:
+        Q, S = oracle.quant_table(synth.table_source(N, K, seed=N * 5 + M))
+        y = qg.w8a16_gemm(dev(x), dev(Q), dev(S))
+        ref = oracle.ref_w8a16(x, Q, S)
+    assert_bounds(host(y), ref, f"{mode} M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("N,Ms", [(16400, (2, 64)), (32784, (40,))])
+def test_w4a16_longest_k_on_wide_outputs(qg, N, Ms):
+    """K = 65536 on wide outputs: 1025 n-tiles make the 512 balanced blocks
+    of up to five tiles (80 KiB of scales per workgroup; 144 KiB of LDS with
+    the partial sums at M = 64), and 2049 n-tiles at M > 32 take the wide
+    kernel, which streams its scales group by group.  Sampled columns (every
+    97th, the edges of the two halves' blocks, the last tile) against the
+    oracle."""
+    K = 65536
+    codes, scales = synth.weights(N, K, seed=N + 65)
+    wp, sp = packed(qg, codes, scales)
+    t1 = min(N // 16 * 10 // 17, 5 * 256) * 16
+    cols = np.unique(np.concatenate([np.arange(0, N, 97), np.arange(t1 - 16, t1 + 16), np.arange(N - 16, N)]))
+    for M in Ms:
+        x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M + N)
+        y = host(qg.w4a16_gemm(dev(x), wp, sp, N))
+        assert_bounds(y[:, cols], oracle.ref_w4a16(x, codes[cols], scales[cols]), f"w4a16 M={M} K={K} N={N}")
+
+
 def test_vocab_workload_full_table(qg):
     """248,320 x 5,120 table: requantised on the device, then the 64-id
     gather (bit-exact) and the M=64 lm_head (sampled columns)."""
