@@ -81,8 +81,9 @@ size_t qg_workspace_bytes(int op, int64_t M, int64_t K, int64_t N);
  *   q      int8 [M][K] out:  q[m][k] = clamp(rne(fp32(x[m][k]) / scale[m]), -127, 127)
  *   scale  fp32 [M]    out:  scale[m] = fp32(max_k |x[m][k]|) / 127 (IEEE division);
  *                            a row of zeros gets scale 0 and codes 0.
- *   M >= 0, K > 0 and K % 128 == 0.  Codes and scales are bit-exact against
- *   that definition.  NaN/Inf inputs give unspecified codes.
+ *   M >= 0, K > 0, K % 128 == 0 and K < 2^31.  Codes and scales are
+ *   bit-exact against that definition.  NaN/Inf inputs give unspecified
+ *   codes.
  */
 int act_quant_int8(const void* x_f16, int64_t M, int64_t K, int64_t ldx,
                    int8_t* q, float* scale, void* stream);
@@ -125,7 +126,10 @@ int w4a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
  *   P[m][n][g] = sum_{j<128} q[m][128g+j] * codes[n][128g+j]   (exact int32)
  *   y[m][n]    = fp16(scale[m] * sum_g fp32(P[m][n][g]) * scales[n][g])   (fp32)
  * Same arguments as w4a16_gemm; the workspace must hold
- * qg_workspace_bytes(QG_OP_W4A8, M, K, N) bytes.
+ * qg_workspace_bytes(QG_OP_W4A8, M, K, N) bytes.  K <= 2^22 (4,194,304):
+ * the kernels address a workgroup's operand block (up to 128 rows of K
+ * codes) with 32-bit buffer offsets; a longer K returns
+ * QG_ERR_UNSUPPORTED_SHAPE.
  */
 int w4a8_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
               const void* w_packed, const void* s_packed, void* y_f16,

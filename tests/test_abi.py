@@ -92,6 +92,15 @@ def test_fp16_activation_gemms_limit_k():
     assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 4, K, 32) > 0
 
 
+def test_w4a8_limits_k():
+    """w4a8_gemm addresses a workgroup's operand block with 32-bit buffer
+    offsets, so K is capped at 2^22."""
+    K = (1 << 22) + 128
+    assert call_gemm("w4a8_gemm", M=4, K=K, N=32, ws=FAKE, wsb=1 << 40) == qg.QG_ERR_UNSUPPORTED_SHAPE
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 4, K, 32) == 2 ** 64 - 1
+    assert qg.qg_workspace_bytes(qg.QG_OP_W4A8, 4, 1 << 22, 32) > 0
+
+
 def test_workspace_errors():
     need = qg.qg_workspace_bytes(qg.QG_OP_W4A8, 64, 5120, 5120)
     assert call_gemm("w4a8_gemm", M=64, K=5120, N=5120, ws=None, wsb=0) == qg.QG_ERR_WORKSPACE

@@ -131,6 +131,11 @@ def test_act_quant_long_rows_take_the_reload_path(qg):
     oq2, os2 = oracle.quant_act(x2)
     assert np.array_equal(host(q2), oq2)
     assert np.array_equal(bits(host(s2)), bits(os2))
+    x3 = synth.acts(1, (1 << 27) + 128, 1.0, 0.01, 20.0, seed=14)   # 2^24 + 16 chunks in one row
+    q3, s3 = qg.act_quant_int8(dev(x3))
+    oq3, os3 = oracle.quant_act(x3)
+    assert np.array_equal(host(q3), oq3)
+    assert np.array_equal(bits(host(s3)), bits(os3))
 
 
 # ---------------------------------------------------------------------------
@@ -214,6 +219,21 @@ def test_w4a8_scales_past_the_lds_budget(qg, M, K, N):
     oq, _ = oracle.quant_act(x)
     assert np.array_equal(host(P).astype(np.int64), oracle.partials(oq, codes[n0:n1])), "int32 partials"
     assert np.array_equal(bits(host(yd)), bits(y))
+
+
+@pytest.mark.parametrize("M,N", [(3, 32), (40, 80), (65, 128)])
+def test_w4a8_at_the_longest_k(qg, M, N):
+    """K = 2^22, the longest w4a8_gemm accepts, in each M regime (two n-tiles
+    per workgroup with the scales carried by the stages, the row split, the
+    128 x 128 tile kernel): codes and token scales bit-exact, the int32
+    partials of a window bit-exact, every output within the fp16 bounds, and
+    the debug call's y bit-identical to the production call's."""
+    K = 1 << 22
+    x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M + 7)
+    codes, scales = synth.weights(N, K, seed=N + 7)
+    _, yd = _w4a8_check(qg, x, codes, scales, window=(0, 3, N - 16, N))
+    wp, sp = packed(qg, codes, scales)
+    assert np.array_equal(bits(host(qg.w4a8_gemm(dev(x), wp, sp, N))), bits(yd))
 
 
 @pytest.mark.slow
