@@ -384,14 +384,18 @@ def test_rmsnorm_prepare_feeds_the_w4a8_gemm(qg):
 
 @pytest.mark.parametrize("T,Hq,Hkv,L", [(1, 8, 8, 1), (1, 4, 1, 300), (5, 24, 4, 37), (5, 24, 4, 1536),
                                         (8, 16, 2, 300), (16, 16, 2, 2000), (16, 24, 4, 16384),
-                                        (3, 6, 3, 8193), (7, 2, 1, 7), (6, 12, 2, 500), (2, 4, 1, 9000)])
+                                        (3, 6, 3, 8193), (7, 2, 1, 7), (6, 12, 2, 500), (2, 4, 1, 9000),
+                                        (16, 4096, 4096, 40), (1, 4096, 32, 300), (16, 8, 1, (1 << 20) + 7)])
 def test_verify_attention_within_bounds(qg, T, Hq, Hkv, L):
     """Against the float64 oracle, element by element, within the fp16 output
     bounds.  Covers one position, GQA groups of 1 to 8 heads, 16 queries x 8
     heads (128 rows: two row tiles per wave), three row tiles (one per wave),
     up to two row tiles (the block's positions split between wave pairs), a
     16k cache (64 splits), 86 and 141 splits (pass 2 loads 64 at a time), a
-    ragged last block and split, and a cache that is only the verify block."""
+    ragged last block and split, a cache that is only the verify block, the
+    most query heads (4096: one split per KV head, 4096 KV heads), 128 query
+    heads per KV head, and a cache of 2^20 + 7 positions (255 splits of 129
+    blocks)."""
     rng = np.random.default_rng(T * 1000 + L)
     q = rng.standard_normal((T, Hq, 256)).astype(np.float16)
     k = rng.standard_normal((L, Hkv, 256)).astype(np.float16)

@@ -84,12 +84,20 @@ def test_vocabulary_width_rows(qg, R, k, p, T):
 
 
 @pytest.mark.parametrize("V,k", [(1, 1), (7, 7), (63, 20), (64, 64), (100, 64), (2049, 33), (2048 * 3 + 5, 64),
-                                 (40967, 20), (8192 * 256, 64)])
+                                 (40967, 20), (8192 * 256, 64),
+                                 # the widest row: 2048 chunks of 8 candidates (the candidate cap)
+                                 (2 ** 24 - 8, 8)])
 def test_ragged_widths(qg, V, k):
     R = 3 if V < 1_000_000 else 1
     x, u = synth.sampler_inputs(R, V, seed=V % 1000, boosted=min(8, V))
     ld = (V + 7) // 8 * 8
     check(run(qg, x, u, k, 0.9, 1.0, ld=ld), oracle.topk_topp_sample(x, k, 0.9, 1.0, u), u, 0.9)
+
+
+def test_most_rows(qg):
+    # R = 65536, the most rows one call takes (narrow rows: one chunk each).
+    x, u = synth.sampler_inputs(65536, 64, seed=11)
+    check(run(qg, x, u, 20, 0.9, 1.0), oracle.topk_topp_sample(x, 20, 0.9, 1.0, u), u, 0.9)
 
 
 @pytest.mark.parametrize("grid", [0.5, 2.0])
