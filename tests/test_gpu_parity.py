@@ -553,7 +553,6 @@ def test_w8a16_ragged_shapes(qg, M, K, N):
     assert_bounds(host(y), oracle.ref_w8a16(x, Q, S))
 
 
-@pytest.mark.slow
 @pytest.mark.parametrize("mode,M,N", [("w4a16", 8, 48), ("w4a16", 40, 48), ("w8a16", 8, 48), ("w8a16", 64, 80)])
 def test_fp16_modes_at_the_longest_k(qg, mode, M, N):
     """K = 65536, the longest w4a16_gemm and w8a16_gemm accept: a workgroup
@@ -594,6 +593,7 @@ def test_w4a16_longest_k_on_wide_outputs(qg, N, Ms):
         assert_bounds(y[:, cols], oracle.ref_w4a16(x, codes[cols], scales[cols]), f"w4a16 M={M} K={K} N={N}")
 
 
+@pytest.mark.slow
 def test_vocab_workload_full_table(qg):
     """248,320 x 5,120 table: requantised on the device, then the 64-id
     gather (bit-exact) and the M=64 lm_head (sampled columns)."""
