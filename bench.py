@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--floor", action="store_true",
                     help="only time the load floors of the decode GEMM's operand walk (qg_probe_read: "
                          "a plain read of its weights, its own access pattern, an empty launch), then exit")
+    ap.add_argument("--vendor", action="store_true",
+                    help="only time the vendor library's plain GEMMs (hipBLASLt through torch: int8, fp8, "
+                         "bf16) at the prefill shape beside this library's W4A8 GEMM, then exit")
     return ap.parse_args()
 
 
@@ -116,6 +119,85 @@ def load_floor():
         print(f"# floor: {name} {out[name]} us", file=sys.stderr, flush=True)
     print(json.dumps({"load_floor_us_per_launch": out, "weight_bytes": wbytes, "code_bytes": cfg["M"] * K,
                       "weight_copies": n}))
+
+
+def vendor_reference():
+    """The vendor library's dense GEMMs at the prefill shape (M = 4096,
+    K = 17408, N = 5120), as context for the W4A8 kernel's matrix-core
+    fraction: torch._int_mm (int8 x int8 -> int32), torch._scaled_mm (fp8
+    e4m3, unit scales, fp16 out) and torch.mm (bf16), each hipBLASLt, with
+    the weight operand [N, K] read transposed and rotated over copies past
+    the Infinity Cache, timed eagerly with HIP events (about 0.4 ms per
+    call, so launch gaps do not count), best of three runs.  Beside them,
+    this library's w4a8_gemm_prepared (the GEMM alone on prepared codes)
+    and w4a8_gemm (quantiser + GEMM), timed the same way.  The vendor GEMMs
+    do no int4 unpack and no per-group rescale."""
+    import torch
+    import spec_verify_amd as qg
+    import synth
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS["prefill_w4a8"]
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    ops = 2.0 * M * N * K
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+
+    def eager_us(fn, n_calls, reps=3):
+        best = float("inf")
+        for _ in range(reps):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(n_calls):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) * 1e3 / n_calls)
+        return best
+
+    out = {}
+
+    def entry(name, fn, n, ncopy, peak):
+        us = eager_us(fn, 4 * n)
+        out[name] = dict(us_per_call=round(us, 2), TOPS=round(ops / us / 1e6, 1),
+                         frac_peak=round(ops / us / 1e6 / peak, 4), weight_copies=ncopy)
+        print(f"# vendor: {name} {out[name]}", file=sys.stderr, flush=True)
+
+    a8 = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=gen)
+    n8 = copies_for(N * K)
+    b8 = [torch.randint(-8, 8, (N, K), dtype=torch.int8, device=dev, generator=gen) for _ in range(n8)]
+    entry("int8_int_mm_hipblaslt", lambda i: torch._int_mm(a8, b8[i % n8].t()), n8, n8, INT8_PEAK_TOPS)
+    del b8
+    fp8 = getattr(torch, "float8_e4m3fn")
+    af = torch.randn((M, K), dtype=torch.float16, device=dev, generator=gen).to(fp8)
+    bf = [torch.randn((N, K), dtype=torch.float16, device=dev, generator=gen).to(fp8) for _ in range(n8)]
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    entry("fp8_e4m3_scaled_mm_hipblaslt",
+          lambda i: torch._scaled_mm(af, bf[i % n8].t(), scale_a=one, scale_b=one, out_dtype=torch.float16),
+          n8, n8, INT8_PEAK_TOPS)
+    del af, bf
+    ab = torch.randn((M, K), dtype=torch.bfloat16, device=dev, generator=gen)
+    n16 = copies_for(N * K * 2)
+    bb = [torch.randn((N, K), dtype=torch.bfloat16, device=dev, generator=gen) for _ in range(n16)]
+    entry("bf16_mm_hipblaslt", lambda i: torch.mm(ab, bb[i % n16].t()), n16, n16, FP16_PEAK_TFLOPS)
+    del ab, bb
+    torch.cuda.empty_cache()
+
+    x, codes, scales = synth.gemm_inputs(cfg)
+    xd = torch.from_numpy(x).to(dev)
+    wp, sp = qg.w4_repack(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    nw = copies_for(wp.numel() + sp.numel() * 2)
+    copies = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(nw - 1)]
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    prep = qg.w4a8_prepare(xd)
+    entry("w4a8_gemm_prepared", lambda i: qg.w4a8_gemm_prepared(prep, M, K, copies[i % nw][0], copies[i % nw][1],
+                                                                 N, y=y), nw, nw, INT8_PEAK_TOPS)
+    ws = torch.empty((qg.qg_workspace_bytes(qg.QG_OP_W4A8, M, K, N),), dtype=torch.uint8, device=dev)
+    entry("w4a8_gemm", lambda i: qg.w4a8_gemm(xd, copies[i % nw][0], copies[i % nw][1], N, y=y, workspace=ws),
+          nw, nw, INT8_PEAK_TOPS)
+    print(json.dumps({"vendor_reference": out, "M": M, "K": K, "N": N}))
 
 
 def gemm_bytes(M, K, N):
@@ -254,6 +336,9 @@ def main():
         return
     if args.floor:
         load_floor()
+        return
+    if args.vendor:
+        vendor_reference()
         return
 
     import numpy as np
