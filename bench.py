@@ -235,8 +235,9 @@ def copies_for(nbytes):
 
 
 def graph_time_us(torch, fn, n_calls, reps=1):
-    """Capture n_calls of fn(i) in a graph, replay `reps` times, return
-    microseconds per call (HIP events on the replay stream)."""
+    """Capture n_calls of fn(i) in a graph, replay it for about 50 ms to
+    warm, then time at least `reps` replays and at least 20 ms of them;
+    return microseconds per call (HIP events on the replay stream)."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -248,10 +249,23 @@ def graph_time_us(torch, fn, n_calls, reps=1):
     with torch.cuda.graph(g):
         for i in range(n_calls):
             fn(i)
-    g.replay()
-    torch.cuda.synchronize()
+    # Warm for about 50 ms of back-to-back replays, then time at least
+    # 20 ms of them: after the idle capture the part takes some milliseconds
+    # to settle (per pair of replays, prefill read 428, 399, then 390-396
+    # us per call; verify at M = 8 18.3, then 21-23 us for about 10 ms,
+    # then 17.8-18.6 us), and a replay of a few calls alone varies by a few
+    # percent.  The decode graphs read the same either way.
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    replay_us = max(e0.elapsed_time(e1) * 1e3, 1.0)
+    for _ in range(min(2000, max(2, int(50e3 / replay_us)))):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(reps, min(2000, int(20e3 / replay_us)))
     e0.record()
     for _ in range(reps):
         g.replay()
