@@ -295,6 +295,33 @@ def test_w4a8_strided_activations(qg):
     assert_bounds(host(y), oracle.ref_w4a8(x, codes, scales))
 
 
+@pytest.mark.parametrize("op,M,K,N", [("w4a8", 40, 640, 160), ("w4a8", 100, 384, 144),
+                                      ("w4a16", 8, 640, 160), ("w4a16", 100, 384, 96), ("w4a16", 40, 256, 32784),
+                                      ("w8a16", 8, 640, 160), ("w8a16", 100, 384, 96)])
+def test_strided_activations_in_every_regime(qg, op, M, K, N):
+    """Activation rows 64 elements apart beyond K (ldx = K + 64): the row
+    split and the 128 x 128 tile kernel for W4A8; the streaming kernel, its
+    64-row chunks past M = 64 and the wide kernel for W4A16; W8A16."""
+    wide = synth.acts(M, K + 64, 1.0, 0.01, 20.0, seed=M + K + N)
+    wide[:, K:] = 30000.0                 # the columns past K must not be read
+    x = np.ascontiguousarray(wide[:, :K])
+    xs = dev(wide)[:, :K]
+    if op == "w8a16":
+        Q, S = oracle.quant_table(synth.table_source(N, K, seed=N + 3))
+        y = qg.w8a16_gemm(xs, dev(Q), dev(S))
+        ref = oracle.ref_w8a16(x, Q, S)
+    else:
+        codes, scales = synth.weights(N, K, seed=N + K)
+        wp, sp = packed(qg, codes, scales)
+        if op == "w4a8":
+            y = qg.w4a8_gemm(xs, wp, sp, N)
+            ref = oracle.ref_w4a8(x, codes, scales)
+        else:
+            y = qg.w4a16_gemm(xs, wp, sp, N)
+            ref = oracle.ref_w4a16(x, codes, scales)
+    assert_bounds(host(y), ref, f"{op} strided M={M} K={K} N={N}")
+
+
 # ---------------------------------------------------------------------------
 # RMSNorm fused with the quantiser
 # ---------------------------------------------------------------------------
