@@ -467,6 +467,15 @@ def extras(torch, qg, synth, np, dev, sections, clocks=False):
         res[name] = dict(M=M, K=K, N=N, us_per_call=round(us, 3), GBps=round(b / us / 1e3, 1),
                          frac_hbm=round(b / us / 1e3 / HBM_PEAK_GBS, 4), TOPS=round(ops / us / 1e6, 2),
                          frac_mfma=round(ops / us / 1e6 / peak_ops, 4), weight_copies=ncopy)
+        if cfg["op"] == "w4a8" and M > 64:
+            # the GEMM alone, on activations quantised once beforehand
+            prep = qg.w4a8_prepare(xd)
+            gus, _ = graph_time_us(torch, lambda i: qg.w4a8_gemm_prepared(prep, M, K, copies[i % ncopy][0],
+                                                                          copies[i % ncopy][1], N, y=y),
+                                   n_calls, reps=2)
+            res[name]["gemm_only"] = dict(us_per_call=round(gus, 3), TOPS=round(ops / gus / 1e6, 2),
+                                          frac_mfma=round(ops / gus / 1e6 / peak_ops, 4))
+            del prep
         if clocks and M > 64:
             # the matrix-core workload: does the part hold its clock under it?
             res[name]["clocks"] = clocks_under_load(torch, gg, max(1, int(3.0 / (us * n_calls * 1e-6))), tries=3)
