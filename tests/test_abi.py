@@ -255,3 +255,34 @@ def test_noalloc_gemm_rejects_shapes_beyond_its_scratch():
     assert f(FAKE, 4, 200, 16, 200, FAKE, FAKE, FAKE, None) == qg.QG_ERR_UNSUPPORTED_SHAPE
     assert f(MIS, 4, 256, 16, 256, FAKE, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
     assert f(None, 4, 256, 16, 256, FAKE, FAKE, FAKE, None) == qg.QG_ERR_INVALID_ARG
+
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With no built library the package import raises; there is no fallback
+    path that could compute anything elsewhere."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "spec_verify_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "spec_verify_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import spec_verify_amd"], cwd=str(tmp_path), capture_output=True,
+                       text=True, env=dict(os.environ, PYTHONPATH=str(tmp_path)), timeout=120)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "is missing" in r.stderr, r.stderr[-2000:]
+
+
+def test_product_sources_never_reference_the_oracle():
+    """The kernels, the C ABI and the binding neither import nor mention the
+    CPU oracle: it is test infrastructure only."""
+    seen = 0
+    for d in ("spec_verify_amd", "include"):
+        for base, _, files in os.walk(os.path.join(ROOT, d)):
+            for f in files:
+                if f.endswith((".py", ".hip", ".cpp", ".h", ".c")):
+                    seen += 1
+                    assert "oracle" not in open(os.path.join(base, f), errors="replace").read().lower(), f
+    assert seen >= 10
