@@ -4,8 +4,8 @@
  *
  * Sources (pages cited by title and section):
  *   [OPT]  "What this repo does that stock vLLM doesn't" (the project's
- *          optimisations page), "In full" items 1, 2, 4, 5 and the section
- *          "int8 prefill for single-user mode".
+ *          optimisations page), "In full" items 1, 2, 4, 5, 6 and the
+ *          section "int8 prefill for single-user mode".
  *   [README] the project README, section "What each step buys".
  *
  * Conventions shared by every entry point
@@ -275,7 +275,7 @@ int w8a16_gemm(const void* x_f16, int64_t M, int64_t K, int64_t N, int64_t ldx,
  *   out     fp16 [T][H]: out[t][h] = fp16(fp32(table[id][h]) * fp32(scales[id][h/128]))
  *           (one rounding: the fp32 product is exact).  An id outside
  *           [0, V) gives a row of zeros.
- *   T >= 0, V > 0, H % 128 == 0.
+ *   T >= 0, V > 0, H % 128 == 0; T, V and H below 2^31.
  */
 int embed_gather_dequant_int8(const int32_t* ids, int64_t T, const int8_t* table,
                               const void* scales_f16, int64_t V, int64_t H,
@@ -288,7 +288,7 @@ int embed_gather_dequant_int8(const int32_t* ids, int64_t T, const int8_t* table
  *   Q     int8 [V][H] out, S fp16 [V][H/128] out:
  *         S = fp16(fp32(absmax of the group) / 127),
  *         Q = clamp(rne(fp32(src) / fp32(S)), -127, 127), and Q = 0 where S == 0.
- *   H % 128 == 0.  Bit-exact against that definition.
+ *   H % 128 == 0; V and H below 2^31.  Bit-exact against that definition.
  */
 int quant_table_int8(const uint16_t* src_bf16, int64_t V, int64_t H,
                      int8_t* Q, void* S_f16, void* stream);
@@ -343,9 +343,8 @@ int qg_selftest_quant_division(unsigned long long* counts, void* stream);
  * (when wgs is a multiple of 8 and wgs / 8 of share, the `share`
  * workgroups reading one slice of a are consecutive on one XCD).  Each
  * thread issues its 16-byte loads 16 at a time, its slice of a first; the
- * only store is one
- * checksum word per wave into sink (device memory, wgs * threads / 64
- * uint32).  a and c are read-only and may alias.  share >= 1, wgs a
+ * only store is one checksum word per wave into sink (device memory,
+ * wgs * threads / 64 uint32).  a and c are read-only and may alias.  share >= 1, wgs a
  * multiple of share, wgs <= 65536; each slice under 2 GiB.  One launch.
  */
 int qg_probe_read(const void* a, int64_t a_bytes, const void* c, int64_t c_bytes, int share, int wgs, int threads,
