@@ -89,10 +89,11 @@ def load_floor():
     """Per-launch times, in a replayed graph, of reads with the decode GEMM's
     operand walk and none of its arithmetic (qg_probe_read): its packed
     weights (13,107,200 B, rotated over copies past the Infinity Cache) read
-    as 256 contiguous slices, then as the row split reads them (64 n-block
-    slices, each read by its four m-groups on one XCD, plus each m-group's
-    quarter of the 327,680 B of codes), and a launch of that grid that reads
-    nothing."""
+    as 256 contiguous slices, then as the row split reads them (128 n-block
+    slices, each read by its two m-groups on one XCD, plus each m-group's
+    half of the 327,680 B of codes), the same with four m-groups per slice
+    (the split of 16-row m-groups over blocks of 5 n-tiles), and a launch of
+    that grid that reads nothing."""
     import torch
     import spec_verify_amd as qg
     import synth
@@ -108,9 +109,11 @@ def load_floor():
     cases = {
         "empty_launch_256x512": lambda i: qg.qg_probe_read(none, None, 1, 256, 512, True, sink),
         "plain_weights_256x640": lambda i: qg.qg_probe_read(w[i % n], None, 1, 256, 640, True, sink),
-        "decode_walk_weights_256x512": lambda i: qg.qg_probe_read(w[i % n], None, 4, 256, 512, True, sink),
-        "decode_walk_256x512": lambda i: qg.qg_probe_read(w[i % n], codes, 4, 256, 512, True, sink),
-        "decode_walk_hot_256x512": lambda i: qg.qg_probe_read(w[0], codes, 4, 256, 512, True, sink),
+        "decode_walk_weights_256x512": lambda i: qg.qg_probe_read(w[i % n], None, 2, 256, 512, True, sink),
+        "decode_walk_256x512": lambda i: qg.qg_probe_read(w[i % n], codes, 2, 256, 512, True, sink),
+        "decode_walk_hot_256x512": lambda i: qg.qg_probe_read(w[0], codes, 2, 256, 512, True, sink),
+        "share4_walk_weights_256x512": lambda i: qg.qg_probe_read(w[i % n], None, 4, 256, 512, True, sink),
+        "share4_walk_256x512": lambda i: qg.qg_probe_read(w[i % n], codes, 4, 256, 512, True, sink),
     }
     out = {}
     for name, fn in cases.items():
@@ -407,7 +410,7 @@ def main():
         max(ncopy, 200))
     kernel_bytes = N * K // 2 + N * (K // 128) * 2 + M * K + M * 4 + M * N * 2
     achieved = kernel_bytes / (gemm_us * 1e-6) / 1e9
-    roofline = dict(bound="hbm", kernel="skinny_kernel<W4A8, 5 n-tiles, 1 m-tile, 8 waves, ring 1> (rows split over 4 workgroups, w4a8_gemm_prepared)", achieved=round(achieved, 1),
+    roofline = dict(bound="hbm", kernel="skinny_kernel<W4A8, 3 n-tiles, 2 m-tiles, 8 waves, ring 1> (n-blocks of 2 or 3 tiles, rows split over 2 workgroups, w4a8_gemm_prepared)", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                     bytes_per_launch=kernel_bytes, avg_launch_us=round(gemm_us, 3), traffic=measured_traffic())
 

@@ -508,8 +508,9 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
 }
 
 // W4A8 at 16 < M <= 64: the streaming kernel with the rows split over
-// workgroups (see launch_skinny).
-constexpr int kMsplitNT = 5, kMsplitPF = 1;
+// workgroups (see launch_skinny): n-blocks of 2 or 3 n-tiles, one or two
+// 16-row m-tiles per workgroup, 8 waves, a one-stage ring.
+constexpr int kMsplitNT = 3, kMsplitNW = 8, kMsplitPF = 1;
 constexpr int kBalancedWgs = 512;   // two workgroups per CU
 
 // Prefetch depth: deep enough to keep several 1 KiB weight blocks per wave
@@ -549,6 +550,19 @@ void launch_mt(const SkinnyParams& p, int mt, dim3 grid, hipStream_t st) {
       default: skinny_kernel<MODE, NT, 4, NW, prefetch_depth<MODE, NT, 4>(), DEBUG, false><<<grid, block, lds, st>>>(p); break;
     }
   }
+}
+
+template <int MT>
+void launch_rowsplit(const SkinnyParams& p, bool dbg, size_t lds, dim3 grid, hipStream_t st) {
+  constexpr int NT = kMsplitNT, NW = kMsplitNW, PF = kMsplitPF;
+  if (dbg && lds)
+    skinny_kernel<kW4A8, NT, MT, NW, PF, true, true><<<grid, dim3(64 * NW), lds, st>>>(p);
+  else if (dbg)
+    skinny_kernel<kW4A8, NT, MT, NW, PF, true, false><<<grid, dim3(64 * NW), 0, st>>>(p);
+  else if (lds)
+    skinny_kernel<kW4A8, NT, MT, NW, PF, false, true><<<grid, dim3(64 * NW), lds, st>>>(p);
+  else
+    skinny_kernel<kW4A8, NT, MT, NW, PF, false, false><<<grid, dim3(64 * NW), 0, st>>>(p);
 }
 
 // Two n-tiles per workgroup only for W4A8 (skinny_plan); every mode takes
@@ -601,33 +615,36 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.ms = 1;
   p.wgs = 0;
   p.t1 = 0;
-  // W4A8 at 16 < M <= 64 (decode batches): one 16-row m-tile and at most
-  // 5 n-tiles per workgroup (the n-tiles dealt into ceil(T / 5) balanced
-  // blocks of 4 or 5), 8 waves splitting K, a one-stage ring.  Each CU then
-  // pulls 82 KB of activation codes and 200 KB of weights at M = 64,
-  // K = N = 5120 (most of them L2 hits, shared by the n-block's m-groups on
-  // one XCD) instead of 327 KB of codes and 82 KB of weights for two
-  // n-tiles x 64 rows, and the loads it keeps in flight stay few; the CU's
-  // limit on outstanding L2 requests is what bounds this GEMM.  Measured at
-  // M = 64, K = N = 5120: 8.2 us (8.8 us with the scales carried by the
-  // stages and a two-barrier reduction), against 10.3 us for an LDS-slab
-  // kernel of two n-tiles x 64 rows with every load in flight at once and
-  // 10.9 us for the streaming kernel's two n-tiles x 64 rows.  A deeper or
-  // earlier-issued ring is slower (9.2-9.7 us).  The debug window runs the
-  // same kernel, instantiated with the partial-sum stores.
+  // W4A8 at 16 < M <= 64 (decode batches): the n-tiles dealt into
+  // ceil(2T / 5) balanced n-blocks of 2 or 3, and each n-block's rows split
+  // into m-groups of one 16-row m-tile (M <= 32) or two (M > 32), so that
+  // M = 17 .. 64 all make two m-groups per n-block at most; 8 waves split K
+  // with a one-stage ring.  Each CU then pulls 164 KB of activation codes
+  // and 82-123 KB of weights at M = 64, K = N = 5120 (mostly L2 hits: the
+  // n-block's two m-groups run on one XCD and share its weights), where one
+  // m-tile over blocks of 4 or 5 n-tiles pulled 82 KB of codes and 200 KB
+  // of weights shared four ways; the CU's limit on outstanding L2 requests
+  // is what bounds this GEMM.  Measured at K = N = 5120: 7.9 us at M = 64
+  // (8.1 us for the layout of 5 n-tiles x 16 rows), 7.4 us at M = 48
+  // (8.1), 6.6 us at M = 17 .. 32 (8.2: that layout left half the CUs
+  // idle), against 10.3 us for an LDS-slab kernel of two n-tiles x 64 rows
+  // with every load in flight at once and 10.9 us for the streaming
+  // kernel's two n-tiles x 64 rows.  One m-tile per workgroup on these
+  // n-blocks (512 workgroups at M = 64) took 9.4 us; 4, 10 or 16 waves
+  // 8.0-8.1 us; a deeper or earlier-issued ring is slower.  Every m-group
+  // of an n-block walks the same groups in the same order, so a row's sum
+  // does not depend on M here.  The debug window runs the same kernel,
+  // instantiated with the partial-sum stores.
   if (a.mode == kW4A8 && a.M > 16) {
-    p.ms = (p.M + 15) / 16;
-    p.wgs = (p.N / 16 + kMsplitNT - 1) / kMsplitNT;
+    const int mtpw = a.M > 32 ? 2 : 1;
+    p.ms = (p.M + 16 * mtpw - 1) / (16 * mtpw);
+    p.wgs = (2 * (p.N / 16) + 4) / 5;
     const dim3 grid((unsigned)(p.wgs * p.ms));
     const size_t lds = w4a8_scale_lds(kMsplitNT, p.G);
-    if (a.dbg && lds)
-      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, true, true><<<grid, dim3(512), lds, st>>>(p);
-    else if (a.dbg)
-      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, true, false><<<grid, dim3(512), 0, st>>>(p);
-    else if (lds)
-      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false, true><<<grid, dim3(512), lds, st>>>(p);
+    if (mtpw == 2)
+      launch_rowsplit<2>(p, a.dbg != nullptr, lds, grid, st);
     else
-      skinny_kernel<kW4A8, kMsplitNT, 1, 8, kMsplitPF, false, false><<<grid, dim3(512), 0, st>>>(p);
+      launch_rowsplit<1>(p, a.dbg != nullptr, lds, grid, st);
     return hipGetLastError();
   }
   const SkinnyPlan pl = skinny_plan(a.mode, a.N, a.K);

@@ -196,16 +196,17 @@ def test_w4a8_row_split_shapes(qg, M, K, N):
     assert np.array_equal(bits(yd), bits(y))
 
 
-@pytest.mark.parametrize("M,K,N", [(40, 32768, 96), (9, 66048, 48), (2, 32896, 16400),
+@pytest.mark.parametrize("M,K,N", [(40, 44032, 96), (20, 44032, 48), (9, 66048, 48), (2, 32896, 16400),
                                    # just inside the budget: 32 KiB of scales beside the row
-                                   # split's 40 KiB of partial sums (72 KiB of LDS)
-                                   (40, 25600, 96)])
+                                   # split's 48 KiB of partial sums at two m-tiles (80 KiB of LDS)
+                                   (40, 43648, 96)])
 def test_w4a8_scales_past_the_lds_budget(qg, M, K, N):
     """K long enough that a workgroup's group scales exceed the 32 KiB the
     weight-streaming kernel stages in LDS, so its stages carry them instead
     (and one shape just inside that budget):
-    the row split (16 < M <= 64), and two and four n-tiles per workgroup
-    (M <= 16, N / 16 up to and past 1024).  The production call against the
+    the row split (16 < M <= 64, three n-tiles and one or two m-tiles per
+    workgroup), and two and four n-tiles per workgroup (M <= 16, N / 16 up
+    to and past 1024).  The production call against the
     oracle (sampled columns on the wide case), and the debug call's partials
     on a window with its y bit-identical to the production call's."""
     x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M * 7 + K)
@@ -718,9 +719,9 @@ def test_rows_do_not_depend_on_the_batch(qg, op):
     """A token's output does not change with the other tokens in the batch,
     bit for bit, within each kernel regime: W4A16 takes the weight-streaming
     kernel at M = 1 .. 64 here; W4A8 takes it at M <= 16 and its row-split
-    form at 16 < M <= 64 (one 16-row m-tile per workgroup, the same group
-    order for every m-tile), which adds the groups in another order than
-    the M <= 16 form."""
+    form at 16 < M <= 64 (one 16-row m-tile per workgroup up to M = 32, two
+    above, over the same n-blocks, with the same group order for every
+    m-tile), which adds the groups in another order than the M <= 16 form."""
     cfg = synth.CONFIGS["decode_w4a8"]
     x, codes, scales = synth.gemm_inputs(cfg)
     wp, sp = packed(qg, codes, scales)

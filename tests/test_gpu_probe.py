@@ -40,7 +40,8 @@ def expected_sink(a, c, share, wgs, threads):
     return out
 
 
-@pytest.mark.parametrize("share,wgs,threads,with_c", [(1, 32, 128, False), (4, 32, 256, True), (4, 24, 192, True)])
+@pytest.mark.parametrize("share,wgs,threads,with_c", [(1, 32, 128, False), (2, 32, 512, True), (4, 32, 256, True),
+                                                    (4, 24, 192, True)])
 def test_probe_reads_its_slices(qg, share, wgs, threads, with_c):
     rng = np.random.default_rng(wgs * 7 + share)
     a = rng.integers(0, 256, size=wgs // share * 16 * 37, dtype=np.uint8)   # slices of 37 chunks
