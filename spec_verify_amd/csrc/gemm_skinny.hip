@@ -511,6 +511,7 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(SkinnyParams p) {
 // workgroups (see launch_skinny): n-blocks of 2 or 3 n-tiles, one or two
 // 16-row m-tiles per workgroup, 8 waves, a one-stage ring.
 constexpr int kMsplitNT = 3, kMsplitNW = 8, kMsplitPF = 1;
+constexpr int kMsplitMinBlocks = 128;   // with two m-groups each, one workgroup per CU
 constexpr int kBalancedWgs = 512;   // two workgroups per CU
 
 // Prefetch depth: deep enough to keep several 1 KiB weight blocks per wave
@@ -616,9 +617,12 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   p.wgs = 0;
   p.t1 = 0;
   // W4A8 at 16 < M <= 64 (decode batches): the n-tiles dealt into
-  // ceil(2T / 5) balanced n-blocks of 2 or 3, and each n-block's rows split
-  // into m-groups of one 16-row m-tile (M <= 32) or two (M > 32), so that
-  // M = 17 .. 64 all make two m-groups per n-block at most; 8 waves split K
+  // ceil(2T / 5) balanced n-blocks of 2 or 3 (at least min(T, 128) blocks,
+  // so that narrow outputs still fill the CUs: at N = 1024, 2048 and 3072
+  // that took M = 64 from 8.1, 8.3 and 8.5 us to 6.4, 6.5 and 7.1 us), and
+  // each n-block's rows split into m-groups of one 16-row m-tile (M <= 32)
+  // or two (M > 32), so that M = 17 .. 64 all make two m-groups per n-block
+  // at most (and the same n-blocks); 8 waves split K
   // with a one-stage ring.  Each CU then pulls 164 KB of activation codes
   // and 82-123 KB of weights at M = 64, K = N = 5120 (mostly L2 hits: the
   // n-block's two m-groups run on one XCD and share its weights), where one
@@ -638,7 +642,7 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
   if (a.mode == kW4A8 && a.M > 16) {
     const int mtpw = a.M > 32 ? 2 : 1;
     p.ms = (p.M + 16 * mtpw - 1) / (16 * mtpw);
-    p.wgs = (2 * (p.N / 16) + 4) / 5;
+    p.wgs = std::max((2 * (p.N / 16) + 4) / 5, std::min(p.N / 16, kMsplitMinBlocks));
     const dim3 grid((unsigned)(p.wgs * p.ms));
     const size_t lds = w4a8_scale_lds(kMsplitNT, p.G);
     if (mtpw == 2)

@@ -179,10 +179,13 @@ def test_w4a8_decode_workload_full(qg):
 
 
 @pytest.mark.parametrize("M,K,N", [(64, 5120, 1024), (48, 5120, 6144), (40, 2560, 144), (64, 2560, 1280),
-                                   (33, 17408, 80), (17, 5120, 16), (64, 128, 96), (20, 384, 36880)])
+                                   (33, 17408, 80), (17, 5120, 16), (64, 128, 96), (20, 384, 36880),
+                                   # narrow outputs: one n-tile per block (the block-count floor)
+                                   (64, 1024, 2048), (32, 1024, 3072)])
 def test_w4a8_row_split_shapes(qg, M, K, N):
     """16 < M <= 64 runs the row-split kernel for every N (n-tiles dealt
-    into balanced blocks of at most 5): the production call against the
+    into balanced blocks of at most 3, at least min(N / 16, 128) of them;
+    one or two m-tiles per workgroup): the production call against the
     oracle, and the debug call's partials on a window that crosses n-block
     edges, with its y bit-identical to the production call's."""
     x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M * 11 + K)
