@@ -675,7 +675,20 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
       launch_mt<kW8A16, 5, 4, false>(p, mt, dim3((unsigned)kBalancedWgs), st);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
+  // Narrow outputs: blocks of pl.nt n-tiles would leave most CUs idle, so
+  // the n-tiles are dealt into at least 256 balanced blocks (fp16-activation
+  // modes) or 128 (W4A8), one n-tile or more each.  W4A16 at M = 8 / 16:
+  // N = 1024 8.6 / 10.0 -> 8.0 / 8.8 us, N = 5120 8.9 / 10.4 -> 8.5 / 9.4 us
+  // (512 blocks: 11.5 / 14.2 us at N = 5120).  W4A8 at M <= 16: N = 1024
+  // 5.4 -> 5.0 us; its 160 two-tile blocks at N = 5120 stay (5.9 us, against
+  // 6.2 us for 256 smaller ones).  The blocks depend on N only, so a row's
+  // sums do not depend on M.
+  dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
+  const int min_blocks = a.mode == kW4A8 ? 128 : 256;
+  if ((int)grid.x < min_blocks) {
+    p.wgs = std::min(p.N / 16, min_blocks);
+    grid = dim3((unsigned)p.wgs);
+  }
   switch (a.mode) {
     case kW4A8:
       return a.dbg ? launch_mode<kW4A8, true>(p, pl, mt, grid, st) : launch_mode<kW4A8, false>(p, pl, mt, grid, st);

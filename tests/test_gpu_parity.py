@@ -254,7 +254,9 @@ def test_w4a8_prefill_workload_sampled(qg):
                                    (65, 256, 144), (100, 512, 272), (129, 384, 128), (200, 128, 16),
                                    # odd group counts per wave, ragged n-blocks, long K, wide N
                                    (7, 2560, 176), (64, 4992, 400), (40, 17408, 96),
-                                   (5, 33024, 32), (4, 256, 16400)])
+                                   (5, 33024, 32), (4, 256, 16400),
+                                   # 254 n-tiles at M <= 16: 127 two-tile blocks become 128 balanced ones
+                                   (9, 256, 4064)])
 def test_w4a8_ragged_shapes(qg, M, K, N):
     x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M + K)
     codes, scales = synth.weights(N, K, seed=N + K)
@@ -511,7 +513,9 @@ def test_w4a16_verify_workload_full(qg, name):
                                    (64, 128, 196624), (40, 256, 196608),
                                    # 1025 and 2560 n-tiles: the 512 balanced blocks, split unevenly
                                    # between the first and second 256 and evenly at the top
-                                   (2, 256, 16400), (16, 128, 40960)])
+                                   (2, 256, 16400), (16, 128, 40960),
+                                   # 1020 n-tiles: 255 four-tile blocks become 256 blocks of up to four
+                                   (8, 256, 16320)])
 def test_w4a16_ragged_shapes(qg, M, K, N):
     x = synth.acts(M, K, 1.0, 0.0, 1.0, seed=M * 3 + K)
     codes, scales = synth.weights(N, K, seed=N * 3 + K)
