@@ -572,7 +572,7 @@ template <int MODE, bool DEBUG>
 hipError_t launch_mode(const SkinnyParams& p, const SkinnyPlan& pl, int mt, dim3 grid, hipStream_t st) {
   if constexpr (MODE == kW4A8) {
     if (pl.nt == 2) {
-      launch_mt<MODE, 2, 8, DEBUG>(p, mt, grid, st);
+      launch_mt<MODE, 2, 4, DEBUG>(p, mt, grid, st);
       return hipGetLastError();
     }
   }
@@ -586,10 +586,12 @@ SkinnyPlan skinny_plan(int mode, int64_t N, int64_t K) {
   (void)K;
   const int64_t ntiles = N / 16;
   SkinnyPlan pl;
-  // Few output tiles (decode-sized N): one or two n-tiles per workgroup with
-  // eight waves splitting K, so enough workgroups exist and each wave has a
-  // short chain of groups.  Many tiles (wide projections, the lm_head): four
-  // n-tiles per workgroup, four waves.
+  // Few output tiles (W4A8 at M <= 16 on decode-sized N): two n-tiles per
+  // workgroup, so enough workgroups exist, and four waves splitting K, each
+  // with a 5-deep ring (at M = 16, N = 5120: 5.5 us against 5.9 us with
+  // eight waves, 5.7 us with two, 5.8 us with a ring of 3 or 4; one n-tile
+  // with eight waves 6.7 us).  Many tiles (wide projections, the lm_head):
+  // four n-tiles per workgroup, four waves.
   if (mode == kW4A8 && ntiles <= 1024)
     pl.nt = 2;
   else
@@ -675,18 +677,20 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
       launch_mt<kW8A16, 5, 4, false>(p, mt, dim3((unsigned)kBalancedWgs), st);
     return hipGetLastError();
   }
-  // Narrow outputs: blocks of pl.nt n-tiles would leave most CUs idle, so
-  // the n-tiles are dealt into at least 256 balanced blocks (fp16-activation
-  // modes) or 128 (W4A8), one n-tile or more each.  W4A16 at M = 8 / 16:
-  // N = 1024 8.6 / 10.0 -> 8.0 / 8.8 us, N = 5120 8.9 / 10.4 -> 8.5 / 9.4 us
-  // (512 blocks: 11.5 / 14.2 us at N = 5120).  W4A8 at M <= 16: N = 1024
-  // 5.4 -> 5.0 us; its 160 two-tile blocks at N = 5120 stay (5.9 us, against
-  // 6.2 us for 256 smaller ones).  The blocks depend on N only, so a row's
-  // sums do not depend on M.
+  // Narrow outputs: blocks of pl.nt n-tiles would leave most CUs idle.
+  // W4A16 / W8A16: where they would make fewer than 256 workgroups, the
+  // n-tiles are dealt into 256 balanced blocks instead (one n-tile or more
+  // each).  At M = 8 / 16: N = 1024 8.6 / 10.0 -> 8.0 / 8.8 us, N = 5120
+  // 8.9 / 10.4 -> 8.5 / 9.4 us (512 blocks: 11.5 / 14.2 us at N = 5120).
+  // W4A8 at M <= 16 gains only from equal blocks: one n-tile per workgroup
+  // up to 256 n-tiles (M = 16: N = 1024 5.0 -> 4.5 us, N = 3072 5.3 ->
+  // 4.8 us), while 128 blocks of one or two tiles took 5.5 us at N = 3072
+  // and 256 of them 5.6 us at N = 5120, where its 160 two-tile blocks stay
+  // (5.5 us).  The blocks depend on N only, so a row's sums do not depend
+  // on M.
   dim3 grid((unsigned)((p.N / 16 + pl.nt - 1) / pl.nt));
-  const int min_blocks = a.mode == kW4A8 ? 128 : 256;
-  if ((int)grid.x < min_blocks) {
-    p.wgs = std::min(p.N / 16, min_blocks);
+  if ((int)grid.x < 256 && (a.mode != kW4A8 || p.N / 16 <= 256)) {
+    p.wgs = std::min(p.N / 16, 256);
     grid = dim3((unsigned)p.wgs);
   }
   switch (a.mode) {

@@ -255,8 +255,8 @@ def test_w4a8_prefill_workload_sampled(qg):
                                    # odd group counts per wave, ragged n-blocks, long K, wide N
                                    (7, 2560, 176), (64, 4992, 400), (40, 17408, 96),
                                    (5, 33024, 32), (4, 256, 16400),
-                                   # 254 n-tiles at M <= 16: 127 two-tile blocks become 128 balanced ones
-                                   (9, 256, 4064)])
+                                   # M <= 16: 254 n-tiles, one per workgroup; 257, blocks of two
+                                   (9, 256, 4064), (9, 256, 4112)])
 def test_w4a8_ragged_shapes(qg, M, K, N):
     x = synth.acts(M, K, 1.0, 0.01, 20.0, seed=M + K)
     codes, scales = synth.weights(N, K, seed=N + K)
